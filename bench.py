@@ -1,0 +1,261 @@
+"""Throughput benchmark: exact attention forward + backward on one MI355X.
+
+One step is one pass of the whole path over one batch: fa_fwd (O, LSE), then
+fa_bwd's three stages (D = rowsum(dO o O), the blocked backward, the dQ
+conversion). The workload is the Llama-2-7B-shaped causal attention layer
+(batch 16, 32 heads, N = 2048, d = 128, bf16; rotary Q/K, dO ~ N(0, 0.01)),
+with inputs resident in device memory before the timed region.
+
+FLOPs follow the pages' accounting: forward 4*B*H*N^2*d, backward
+10*B*H*N^2*d (the recompute of S included), halved under the causal mask.
+
+Prints ONE JSON line. Besides the required keys it carries:
+  roofline      the dominant kernel (backward main) against the bf16 dense MFMA
+                peak, its duration measured with HIP events on the launch
+                stream inside the timed region; HBM traffic from the committed
+                rocprofv3 counter summary when it was taken on the current
+                kernel source, else null;
+  cpu_baseline  the fp64 oracle timed on host cores on a sample of the same
+                workload (also used as a parity spot-check of the timed run);
+  sweep         forward and forward+backward TFLOPS for bf16 d = 128 at
+                N = 2048, 4096, 8192 (B*N = 16384 tokens, 16 heads).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOPS (fwd; fwd+bwd) bf16 d=128 N=2k–8k, % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_c5_traffic.json")
+BWD_SRC = os.path.join(ROOT, "exact_attention_34_amd", "csrc", "fa_bwd.hip")
+
+
+def _src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic():
+    """Per-launch HBM bytes of the backward main kernel from the committed
+    counter summary, or None if absent or taken on other kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != _src_hash(BWD_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _inputs(w, torch, dev):
+    import attn_inputs as ai
+    inp = ai.make_inputs(w)
+    return {k: v.to(dev) for k, v in inp.items()}, inp
+
+
+def _step_fns(fa, torch, w, d):
+    B, H, N, D = w.B, w.H, w.N, w.d
+    o = torch.empty_like(d["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=d["q"].device)
+    dq, dk, dv = (torch.empty_like(d["q"]) for _ in range(3))
+    dvec = torch.empty((B, H, N), dtype=torch.float32, device=d["q"].device)
+    acc = torch.empty((B, H, N, D), dtype=torch.float32, device=d["q"].device)
+    L = fa.lib()
+    code = {torch.bfloat16: fa.BF16, torch.float16: fa.F16}[d["q"].dtype]
+    P = lambda t: t.data_ptr()
+    st = torch.cuda.current_stream().cuda_stream
+    c = int(w.causal)
+
+    def ck(rc):
+        if rc != 0:
+            raise fa.FAError("bench", rc)
+
+    def fwd():
+        ck(L.fa_fwd(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), w.scale, c, P(o),
+                    P(lse), st))
+
+    def pre():
+        ck(L.fa_bwd_preprocess(code, B, H, N, D, P(o), P(d["do"]), P(dvec), P(acc), st))
+
+    def main():
+        ck(L.fa_bwd_main(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(d["do"]),
+                         P(lse), P(dvec), w.scale, c, P(acc), P(dk), P(dv), st))
+
+    def conv():
+        ck(L.fa_bwd_dq_convert(code, B, H, N, D, P(acc), w.scale, P(dq), st))
+
+    return (fwd, pre, main, conv), {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def time_workload(fa, torch, w, steps, warmup, per_kernel=True):
+    """Returns (ms_per_step, ms_fwd_only, per-kernel ms dict, outputs, host inputs)."""
+    d, host = _inputs(w, torch, "cuda")
+    fns, outs = _step_fns(fa, torch, w, d)
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    names = ("fwd", "bwd_preprocess", "bwd_main", "bwd_dq_convert")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(steps):
+        for i, f in enumerate(fns):
+            if per_kernel:
+                ev[s][i].record()
+            f()
+        if per_kernel:
+            ev[s][-1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    kern = None
+    if per_kernel:
+        kern = {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+                for i, n in enumerate(names)}
+    # forward alone
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(steps):
+        fns[0]()
+    f1.record()
+    torch.cuda.synchronize()
+    ms_fwd = f0.elapsed_time(f1) / steps
+    # one clean step so the outputs correspond to the inputs
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    return ms_step, ms_fwd, kern, outs, host
+
+
+def slice_errors(outs, b, h, o_ref, lse_ref, g):
+    """Errors of the timed run's outputs on one slice against the oracle."""
+    import numpy as np
+
+    def a(t):
+        return t[b, h].detach().cpu().double().numpy()
+
+    def rel(x, ref):
+        return float(np.linalg.norm(x - ref) / np.linalg.norm(ref))
+
+    return {"o_max_abs": float(np.abs(a(outs["o"]) - o_ref).max()),
+            "o_rel_l2": rel(a(outs["o"]), o_ref),
+            "lse_max_abs": float(np.abs(a(outs["lse"]) - lse_ref).max()),
+            "dq_rel_l2": rel(a(outs["dq"]), g["dq"]),
+            "dk_rel_l2": rel(a(outs["dk"]), g["dk"]),
+            "dv_rel_l2": rel(a(outs["dv"]), g["dv"])}
+
+
+def cpu_baseline(w, host, outs, min_seconds=10.0, max_slices=8):
+    """The fp64 oracle on whole (batch, head) slices of the same workload,
+    until min_seconds of work; also compares those slices with the GPU run."""
+    import oracle
+    t_total, n, errs = 0.0, 0, []
+    slices = [(b, h) for b in (0, w.B - 1) for h in (0, w.H - 1)]
+    slices += [(b, h) for b in range(w.B) for h in range(w.H) if (b, h) not in slices]
+    for b, h in slices[:max_slices]:
+        q, k, v, do = (host[x][b, h].double().numpy() for x in ("q", "k", "v", "do"))
+        t = time.perf_counter()
+        o_ref, lse_ref = oracle.attention_fwd(q, k, v, w.scale, w.causal)
+        g = oracle.attention_bwd(q, k, v, do, w.scale, w.causal)
+        t_total += time.perf_counter() - t
+        n += 1
+        errs.append(slice_errors(outs, b, h, o_ref, lse_ref, g))
+        if t_total >= min_seconds:
+            break
+    flops = n * (w.fwd_flops() + w.bwd_flops()) / (w.B * w.H)
+    worst = {k: max(e[k] for e in errs) for k in errs[0]}
+    return {"value": flops / t_total / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d (batch, head) slices of the workload, fwd+bwd in fp64 "
+                      "(%.1f s)" % (n, w.B * w.H, t_total)}, worst
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c5")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
+    ap.add_argument("--no-sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path has no multi-GPU mode "
+              "(each (batch, head) slice is independent; see the sharding notes). "
+              "Run with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import attn_inputs as ai
+    import exact_attention_34_amd as fa
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fa.lib()
+
+    w = ai.WORKLOADS[args.workload]
+    ms_step, ms_fwd, kern, outs, host = time_workload(fa, torch, w, args.steps, args.warmup)
+    flops_step = w.fwd_flops() + w.bwd_flops()
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    fwd_tflops = w.fwd_flops() / (ms_fwd * 1e-3) / 1e12
+
+    main_ms = kern["bwd_main"]
+    main_flops = w.bwd_flops()
+    achieved = main_flops / (main_ms * 1e-3) / 1e12
+    traffic = _traffic()
+    roofline = {"kernel": "bwd_main_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "ms_per_launch": round(main_ms, 4),
+                "flops_per_launch": main_flops}
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if w.dtype == "bf16" else w.dtype,
+           "data": "synthetic (seeded N(0,1) inputs, rotary Q/K, dO ~ N(0,0.01))",
+           "config": {"workload": "%s: %s" % (w.name, w.note), "B": w.B, "H": w.H, "N": w.N,
+                      "d": w.d, "causal": w.causal, "global_batch": w.B, "seq_len": w.N,
+                      "parallelism": "none (1 GPU)"},
+           "fwd_tflops": round(fwd_tflops, 2),
+           "fwd_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+           "fwdbwd_frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+           "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+           "roofline": roofline}
+
+    if not args.no_cpu:
+        cb, worst = cpu_baseline(w, host, outs)
+        out["cpu_baseline"] = cb
+        out["parity_spot_check"] = worst
+    if not args.no_sweep:
+        sweep = []
+        for name in ("perf-2k", "perf-4k", "perf-8k", "perf-2k-causal", "perf-4k-causal",
+                     "perf-8k-causal"):
+            ws = ai.WORKLOADS[name]
+            s_ms, f_ms, _, _, _ = time_workload(fa, torch, ws, 10, 3, per_kernel=False)
+            tf = (ws.fwd_flops() + ws.bwd_flops()) / (s_ms * 1e-3) / 1e12
+            ff = ws.fwd_flops() / (f_ms * 1e-3) / 1e12
+            sweep.append({"workload": name, "B": ws.B, "H": ws.H, "N": ws.N,
+                          "causal": ws.causal, "fwd_tflops": round(ff, 1),
+                          "fwdbwd_tflops": round(tf, 1),
+                          "fwd_frac": round(ff / PEAK_BF16_TFLOPS, 4),
+                          "fwdbwd_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+            print("# sweep %s fwd %.1f TFLOPS fwd+bwd %.1f TFLOPS" % (name, ff, tf),
+                  file=sys.stderr, flush=True)
+        out["sweep"] = sweep
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

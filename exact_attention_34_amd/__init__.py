@@ -1,0 +1,150 @@
+"""Exact attention (forward and recompute backward) on AMD MI355X.
+
+A thin ctypes binding over ``libfa.so``, whose C ABI is declared in
+``include/fa.h``. This module only marshals arguments: it checks tensors,
+allocates the outputs with torch on the tensors' device, and passes raw
+pointers plus torch's current HIP stream to the library. Every step of the
+computation runs in the library's HIP kernels; there is no other code path.
+If the library has not been built, every call raises.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_main", "bwd_dq_convert",
+           "bwd_workspace_bytes", "FAError", "library_path", "lib",
+           "F32", "F16", "BF16"]
+
+F32, F16, BF16 = 0, 1, 2
+_CODES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, fn, code):
+        msg = lib().fa_status_str(code).decode() if _lib is not None else str(code)
+        super().__init__("%s failed: %s (%d)" % (fn, msg, code))
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libfa.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libfa.so is not built; run __graft_entry__.build() "
+                          "(or python exact_attention_34_amd/build.py)")
+    L = ctypes.CDLL(_LIB_PATH)
+    i, f, p, z = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    L.fa_abi_version.restype = i
+    L.fa_status_str.argtypes = [i]
+    L.fa_status_str.restype = ctypes.c_char_p
+    L.fa_fwd.argtypes = [i, i, i, i, i, p, p, p, f, i, p, p, p]
+    L.fa_fwd.restype = i
+    L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.fa_bwd_workspace_bytes.restype = z
+    L.fa_bwd.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, p, p, z, p]
+    L.fa_bwd.restype = i
+    L.fa_bwd_preprocess.argtypes = [i, i, i, i, i, p, p, p, p, p]
+    L.fa_bwd_preprocess.restype = i
+    L.fa_bwd_main.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, p, p]
+    L.fa_bwd_main.restype = i
+    L.fa_bwd_dq_convert.argtypes = [i, i, i, i, i, p, f, p, p]
+    L.fa_bwd_dq_convert.restype = i
+    _lib = L
+    return L
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_qkv(*ts):
+    t0 = ts[0]
+    if t0.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in ts:
+        if t.shape != t0.shape or t.dtype != t0.dtype or t.device != t0.device:
+            raise ValueError("tensors must share shape, dtype and device")
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if t0.dtype not in _CODES:
+        raise ValueError("unsupported dtype %s" % t0.dtype)
+    return (_CODES[t0.dtype],) + tuple(t0.shape)
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def _call(fn, *args):
+    rc = getattr(lib(), fn)(*args)
+    if rc != 0:
+        raise FAError(fn, rc)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def fwd(q, k, v, scale=None, causal=False):
+    """O, LSE = attention(q, k, v). q, k, v: [B, H, N, d] on the GPU."""
+    dt, B, H, N, d = _check_qkv(q, k, v)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _call("fa_fwd", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _scale(scale, d),
+          int(bool(causal)), _ptr(o), _ptr(lse), _stream(q))
+    return o, lse
+
+
+def bwd_workspace_bytes(dtype, B, H, N, d):
+    return int(lib().fa_bwd_workspace_bytes(_CODES[dtype], B, H, N, d))
+
+
+def bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None):
+    """dQ, dK, dV of attention given dO, and O, LSE from fwd()."""
+    dt, B, H, N, d = _check_qkv(q, k, v, o, do)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    nbytes = bwd_workspace_bytes(q.dtype, B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _call("fa_bwd", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+          _ptr(lse), _scale(scale, d), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+    return dq, dk, dv
+
+
+def bwd_preprocess(o, do, dvec, dq_acc):
+    """Stage 1 of bwd: dvec = rowsum(dO o O) (fp32 [B,H,N]), dq_acc = 0."""
+    dt, B, H, N, d = _check_qkv(o, do)
+    _call("fa_bwd_preprocess", dt, B, H, N, d, _ptr(o), _ptr(do), _ptr(dvec),
+          _ptr(dq_acc), _stream(o))
+
+
+def bwd_main(q, k, v, do, lse, dvec, dq_acc, dk, dv, scale=None, causal=False):
+    """Stage 2 of bwd: dK, dV, and dq_acc += unscaled dS K."""
+    dt, B, H, N, d = _check_qkv(q, k, v, do, dk, dv)
+    _call("fa_bwd_main", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+          _ptr(dvec), _scale(scale, d), int(bool(causal)), _ptr(dq_acc), _ptr(dk),
+          _ptr(dv), _stream(q))
+
+
+def bwd_dq_convert(dq_acc, dq, scale=None):
+    """Stage 3 of bwd: dq = dtype(scale * dq_acc)."""
+    dt, B, H, N, d = _check_qkv(dq)
+    _call("fa_bwd_dq_convert", dt, B, H, N, d, _ptr(dq_acc), _scale(scale, d), _ptr(dq),
+          _stream(dq))

@@ -1,0 +1,133 @@
+// fa_api.hip -- the C ABI declared in include/fa.h: argument checks, workspace
+// layout and dispatch to the kernel launchers. Nothing here allocates, frees
+// or synchronises; every launch goes to the caller's stream.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 16;
+constexpr size_t kWsAlign = 256;
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Checks shared by every entry point. Returns FA_OK or an error code.
+int check_shape(int dtype, int B, int H, int N, int d, bool bwd) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  const long long elems = (long long)B * H * N * d;
+  if (elems >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (bwd && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int check_scale_causal(float scale, int causal) {
+  if (!(isfinite(scale) && scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+bool tensor_ok(const void *p) { return p != nullptr && aligned(p, kAlign); }
+bool vec_ok(const void *p) { return p != nullptr && aligned(p, 4); }
+
+int status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+size_t d_bytes(int B, int H, int N) { return round_up((size_t)B * H * N * sizeof(float), kWsAlign); }
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char *fa_status_str(int s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head size or dtype";
+    case FA_ERR_WORKSPACE: return "workspace too small";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
+           float scale, int causal, void *O, float *LSE, void *stream) {
+  int rc = check_shape(dtype, B, H, N, d, false);
+  if (rc != FA_OK) return rc;
+  if ((rc = check_scale_causal(scale, causal)) != FA_OK) return rc;
+  if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O) || !vec_ok(LSE))
+    return FA_ERR_INVALID_ARG;
+  return status(fa::launch_fwd(dtype, B, H, N, d, Q, K, V, scale, causal, O, LSE,
+                               (hipStream_t)stream));
+}
+
+size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d) {
+  if (check_shape(dtype, B, H, N, d, true) != FA_OK) return 0;
+  return d_bytes(B, H, N) + (size_t)B * H * N * d * sizeof(float);
+}
+
+int fa_bwd_preprocess(int dtype, int B, int H, int N, int d, const void *O, const void *dO,
+                      float *Dvec, float *dQacc, void *stream) {
+  const int rc = check_shape(dtype, B, H, N, d, true);
+  if (rc != FA_OK) return rc;
+  if (!tensor_ok(O) || !tensor_ok(dO) || !vec_ok(Dvec) || !tensor_ok(dQacc))
+    return FA_ERR_INVALID_ARG;
+  return status(fa::launch_bwd_preprocess(dtype, B, H, N, d, O, dO, Dvec, dQacc,
+                                          (hipStream_t)stream));
+}
+
+int fa_bwd_main(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                const void *V, const void *dO, const float *LSE, const float *Dvec,
+                float scale, int causal, float *dQacc, void *dK, void *dV, void *stream) {
+  int rc = check_shape(dtype, B, H, N, d, true);
+  if (rc != FA_OK) return rc;
+  if ((rc = check_scale_causal(scale, causal)) != FA_OK) return rc;
+  if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(dO) || !vec_ok(LSE) ||
+      !vec_ok(Dvec) || !tensor_ok(dQacc) || !tensor_ok(dK) || !tensor_ok(dV))
+    return FA_ERR_INVALID_ARG;
+  return status(fa::launch_bwd_main(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
+                                    dQacc, dK, dV, (hipStream_t)stream));
+}
+
+int fa_bwd_dq_convert(int dtype, int B, int H, int N, int d, const float *dQacc, float scale,
+                      void *dQ, void *stream) {
+  const int rc = check_shape(dtype, B, H, N, d, true);
+  if (rc != FA_OK) return rc;
+  if (!(isfinite(scale) && scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (!tensor_ok(dQacc) || !tensor_ok(dQ)) return FA_ERR_INVALID_ARG;
+  return status(fa::launch_bwd_dq_convert(dtype, B, H, N, d, dQacc, scale, dQ,
+                                          (hipStream_t)stream));
+}
+
+int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
+           const void *O, const void *dO, const float *LSE, float scale, int causal, void *dQ,
+           void *dK, void *dV, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shape(dtype, B, H, N, d, true);
+  if (rc != FA_OK) return rc;
+  if ((rc = check_scale_causal(scale, causal)) != FA_OK) return rc;
+  if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O) || !tensor_ok(dO) ||
+      !vec_ok(LSE) || !tensor_ok(dQ) || !tensor_ok(dK) || !tensor_ok(dV) ||
+      !tensor_ok(workspace))
+    return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_bwd_workspace_bytes(dtype, B, H, N, d)) return FA_ERR_WORKSPACE;
+  float *Dvec = (float *)workspace;
+  float *dQacc = (float *)((char *)workspace + d_bytes(B, H, N));
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = status(fa::launch_bwd_preprocess(dtype, B, H, N, d, O, dO, Dvec, dQacc, st))) !=
+      FA_OK)
+    return rc;
+  if ((rc = status(fa::launch_bwd_main(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
+                                       dQacc, dK, dV, st))) != FA_OK)
+    return rc;
+  return status(fa::launch_bwd_dq_convert(dtype, B, H, N, d, dQacc, scale, dQ, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// fa_device.h -- gfx950 device helpers for the attention kernels: vector
+// types, the MFMA instructions used, 16-bit packing with round-to-nearest-even,
+// the lane exchange across wave halves, and the XCD-aware tile order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16-bit element tags.
+struct BF16 {};
+struct F16 {};
+
+// D(32x32 fp32) += A(32x16) * B(16x32), both 16-bit. Operand layout per lane l
+// (wave64): A row l%32, k = 8*(l/32)..+7; B column l%32, same k.
+// C/D: column l%32, rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+template <typename T>
+__device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c);
+
+template <>
+__device__ __forceinline__ f32x16 mfma32<BF16>(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<F16>(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 -> one dword of two 16-bit values (lo = a), round to nearest even.
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float a, float b);
+template <>
+__device__ __forceinline__ uint32_t pack2<BF16>(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
+  f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 16-bit -> fp32.
+template <typename T>
+__device__ __forceinline__ float to_f32(uint16_t h);
+template <>
+__device__ __forceinline__ float to_f32<BF16>(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+template <>
+__device__ __forceinline__ float to_f32<F16>(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Low / high 16-bit halves of two dwords, paired into one dword.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Reductions over the lane pair (l, l ^ 32). v_permlane32_swap exchanges
+// lanes 32-63 of its first operand with lanes 0-31 of its second; with both
+// operands equal to x, one result holds x[l] and the other x[l ^ 32] in every
+// lane, so combining the two results reduces the pair.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Swap bits 2 and 3 of a key index inside its 16-block. Row r of a 32x32
+// MFMA result lives in lane group (r >> 2) & 1 at register slot
+// 4 * (r >> 3) + (r & 3); storing the contraction operand of the next product
+// in this order lets each lane read its 8 k-slots as one 16-byte word.
+__device__ __forceinline__ int swap23(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2). Map the linear workgroup id so that consecutive tile ids -- the tiles
+// of one (batch, head) slice, which share K and V -- run on the same XCD.
+__device__ __forceinline__ int xcd_tile(int wg, int total) {
+  constexpr int kXcd = 8;
+  const int q = total / kXcd, r = total % kXcd;
+  const int x = wg % kXcd, k = wg / kXcd;
+  return (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
+__device__ __forceinline__ u32x4 ld128(const void *p) { return *(const u32x4 *)p; }
+__device__ __forceinline__ void st128(void *p, const u32x4 &v) { *(u32x4 *)p = v; }
+
+}  // namespace fa

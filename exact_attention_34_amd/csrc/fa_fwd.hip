@@ -1,0 +1,408 @@
+// fa_fwd.hip -- forward pass of exact attention on gfx950.
+//
+// One workgroup computes BR query rows of one (batch, head) slice and sweeps
+// the key/value tiles once ("Flash Attention" notes, section 1: Q blocks in
+// the outer loop, K/V blocks in the inner one; section 2, part 4.2: the
+// forward loop). Per tile it keeps the running row max m and normaliser l and
+// rescales the unnormalised output O~ by exp(m_old - m_new) (section 2,
+// parts 3.1 and 4.1, the two-block merges), so no N x N array is formed; the
+// division by l is deferred to the end and LSE = m + log l is returned for
+// the backward (section 3, part 3).
+//
+// Work is done in base 2: scores are scaled by scale * log2(e) so that one
+// v_exp_f32 (2^x) gives each exponential, and m is kept in those units.
+//
+// Data flow per wave (32 query rows, 16-bit inputs):
+//   * Q rows stay in VGPRs for the whole sweep, as the B operand of
+//     S^T = K Q^T (v_mfma_f32_32x32x16_{bf16,f16}); lane l owns query row
+//     l % 32, so a row's 64 tile scores sit in two lanes (l and l ^ 32).
+//   * Row max and row sum are in-register reductions plus one
+//     v_permlane32_swap between the wave halves.
+//   * P, rounded to the input type, is the B operand of O~^T += V^T P^T
+//     straight from registers; V^T comes from LDS.
+//   * K (row-major) and V^T tiles are double-buffered in LDS: the global
+//     loads of tile j+1 are issued before the MFMAs of tile j and written to
+//     the other buffer after them, one barrier per tile.
+// The fp32 variant is the same loop on v_mfma_f32_32x32x2_f32 with P kept in
+// fp32.
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int kThreads = 256;  // 4 waves
+  static constexpr int BR = 128;        // query rows per workgroup, 32 per wave
+  static constexpr int BC = 64;         // keys per tile
+  static constexpr int KS = D + 8;      // K tile row stride (16-bit elements)
+  static constexpr int VS = BC + 8;     // V^T tile row stride
+  static constexpr int KTILE = BC * KS;
+  static constexpr int VTILE = D * VS;
+  static constexpr int NCH = D / 16;    // 16-wide k chunks of q . k
+  static constexpr int NDT = D / 32;    // 32-wide output column tiles
+  static constexpr int TPR = D / 8;     // threads per row in a 16-byte-chunk load
+  static constexpr int KCH = (BC * D / 8) / kThreads;  // 16-byte chunks per thread per tile
+  static_assert(KCH == 2 || KCH == 4, "tile split");
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int N,
+    int nqb, int total, float c2) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (C::KTILE + C::VTILE)];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int bh = tile / nqb;
+  int qb = tile - bh * nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
+  const int q0 = qb * C::BR;
+  const int wq0 = q0 + 32 * w;  // first query row of this wave
+  const int qrow = wq0 + l32;
+  const size_t base = (size_t)bh * N * D;
+  const uint16_t *Qh = Q + base, *Kh = K + base, *Vh = V + base;
+
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  u32x4 qreg[C::NCH];
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c)
+    qreg[c] = (qrow < N) ? ld128(Qh + (size_t)qrow * D + 16 * c + 8 * g) : zero4;
+
+  const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
+  const int ntiles = (kend + C::BC - 1) / C::BC;
+
+  // Global -> register prefetch of one K/V tile.
+  u32x4 kpre[C::KCH], vpre[C::KCH];
+  const int vk0 = C::KCH * (tid / C::TPR);  // first of this thread's V keys
+  const int vd0 = 8 * (tid % C::TPR);       // first of its 8 columns
+  auto gload = [&](int kt) {
+    const int kb = kt * C::BC;
+#pragma unroll
+    for (int r = 0; r < C::KCH; ++r) {
+      const int c = tid + C::kThreads * r;
+      const int key = kb + c / C::TPR, col = 8 * (c % C::TPR);
+      kpre[r] = (key < N) ? ld128(Kh + (size_t)key * D + col) : zero4;
+    }
+#pragma unroll
+    for (int r = 0; r < C::KCH; ++r) {
+      const int key = kb + vk0 + r;
+      vpre[r] = (key < N) ? ld128(Vh + (size_t)key * D + vd0) : zero4;
+    }
+  };
+  // Register -> LDS: K row-major, V transposed with keys in swap23 order.
+  auto swrite = [&](int buf) {
+    uint16_t *Ks = lds + buf * (C::KTILE + C::VTILE);
+    uint16_t *Vt = Ks + C::KTILE;
+#pragma unroll
+    for (int r = 0; r < C::KCH; ++r) {
+      const int c = tid + C::kThreads * r;
+      st128(Ks + (c / C::TPR) * C::KS + 8 * (c % C::TPR), kpre[r]);
+    }
+    const int p0 = swap23(vk0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int h = e >> 1;
+      uint16_t *dst = Vt + (vd0 + e) * C::VS + p0;
+      if constexpr (C::KCH == 4) {
+        u32x2 v;
+        v[0] = (e & 1) ? pair_hi(vpre[0][h], vpre[1][h]) : pair_lo(vpre[0][h], vpre[1][h]);
+        v[1] = (e & 1) ? pair_hi(vpre[2][h], vpre[3][h]) : pair_lo(vpre[2][h], vpre[3][h]);
+        *(u32x2 *)dst = v;
+      } else {
+        *(uint32_t *)dst =
+            (e & 1) ? pair_hi(vpre[0][h], vpre[1][h]) : pair_lo(vpre[0][h], vpre[1][h]);
+      }
+    }
+  };
+
+  f32x16 o[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m_run = -INFINITY;  // running max of scaled scores (base-2 units)
+  float l_run = 0.f;        // this lane's share of the running normaliser
+
+  gload(0);
+  swrite(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) gload(kt + 1);
+    __syncthreads();
+    const uint16_t *Ks = lds + buf * (C::KTILE + C::VTILE);
+    const uint16_t *Vt = Ks + C::KTILE;
+    const int kb = kt * C::BC;
+    // Under the causal mask a wave whose rows all precede the tile skips it.
+    if (!CAUSAL || kb <= wq0 + 31) {
+      f32x16 s[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < C::NCH; ++c) {
+          const u32x4 a = ld128(Ks + (32 * t + l32) * C::KS + 16 * c + 8 * g);
+          s[t] = mfma32<T>(a, qreg[c], s[t]);
+        }
+      }
+      // scale to base 2, mask, tile row max
+      const bool need_mask = (kb + C::BC > N) || (CAUSAL && kb + C::BC - 1 > wq0);
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[t][r] * c2;
+          if (need_mask) {
+            const int key = kb + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key >= N || (CAUSAL && key > qrow)) x = -INFINITY;
+          }
+          s[t][r] = x;
+          mloc = fmaxf(mloc, x);
+        }
+      mloc = pair_max(mloc);
+      const float m_new = fmaxf(m_run, mloc);
+      const float mb = (m_new == -INFINITY) ? 0.f : m_new;  // never form -inf - -inf
+      const float alpha = fast_exp2(m_run - mb);
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(s[t][r] - mb);
+          s[t][r] = p;
+          psum += p;
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      // Rescale O~ only when some row's max moved (alpha == 1 otherwise).
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      // P as B operand: 16-key chunk cc of subtile t = registers 8cc..8cc+7.
+      u32x4 pp[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            pp[t][cc][h] = pack2<T>(s[t][8 * cc + 2 * h], s[t][8 * cc + 2 * h + 1]);
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const u32x4 a = ld128(Vt + (32 * dt + l32) * C::VS + 32 * t + 16 * cc + 8 * g);
+            o[dt] = mfma32<T>(a, pp[t][cc], o[dt]);
+          }
+    }
+    if (kt + 1 < ntiles) swrite(buf ^ 1);
+  }
+
+  // Epilogue: O = O~ / l, LSE = (m + log2 l) * ln 2.
+  const float l_tot = pair_sum(l_run);
+  const float inv = fast_rcp(l_tot);
+  if (qrow < N) {
+    uint16_t *Orow = O + base + (size_t)qrow * D;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 v;
+        v[0] = pack2<T>(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv);
+        v[1] = pack2<T>(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
+        *(u32x2 *)(Orow + 32 * dt + 8 * i + 4 * g) = v;
+      }
+    if (g == 0) LSE[(size_t)bh * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+// fp32 inputs: the same sweep on v_mfma_f32_32x32x2_f32 (A: one value per
+// lane, row l % 32, k = l / 32), 32-key tiles, single-buffered LDS.
+template <int D>
+struct FwdF32Cfg {
+  static constexpr int kThreads = 256;
+  static constexpr int BR = 128;
+  static constexpr int BC = 32;
+  static constexpr int KS = D + 2;  // bank-conflict-free A reads of K
+  static constexpr int VS = D + 8;  // lane groups 0/1 read rows 4 apart: 4*VS = 32 mod 64 banks
+  static constexpr int NDT = D / 32;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fwd_f32_kernel(
+    const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
+    float *__restrict__ O, float *__restrict__ LSE, int N, int nqb, int total, float c2) {
+  using C = FwdF32Cfg<D>;
+  __shared__ float Ks[C::BC * C::KS];
+  __shared__ float Vs[C::BC * C::VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int bh = tile / nqb;
+  int qb = tile - bh * nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;
+  const int q0 = qb * C::BR;
+  const int wq0 = q0 + 32 * w;
+  const int qrow = wq0 + l32;
+  const size_t base = (size_t)bh * N * D;
+  const float *Qh = Q + base, *Kh = K + base, *Vh = V + base;
+
+  float qreg[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) qreg[c] = (qrow < N) ? Qh[(size_t)qrow * D + 2 * c + g] : 0.f;
+
+  const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
+  const int ntiles = (kend + C::BC - 1) / C::BC;
+  f32x16 o[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int kb = kt * C::BC;
+    __syncthreads();
+    for (int e = tid; e < C::BC * D / 4; e += C::kThreads) {
+      const int row = e / (D / 4), col = 4 * (e % (D / 4));
+      const int key = kb + row;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (key < N) {
+        kv = *(const f32x4 *)(Kh + (size_t)key * D + col);
+        vv = *(const f32x4 *)(Vh + (size_t)key * D + col);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        Ks[row * C::KS + col + u] = kv[u];
+        Vs[row * C::VS + col + u] = vv[u];
+      }
+    }
+    __syncthreads();
+    if (CAUSAL && kb > wq0 + 31) continue;
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c)
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[l32 * C::KS + 2 * c + g], qreg[c], s, 0, 0, 0);
+    const bool need_mask = (kb + C::BC > N) || (CAUSAL && kb + C::BC - 1 > wq0);
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[r] * c2;
+      if (need_mask) {
+        const int key = kb + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (key >= N || (CAUSAL && key > qrow)) x = -INFINITY;
+      }
+      s[r] = x;
+      mloc = fmaxf(mloc, x);
+    }
+    mloc = pair_max(mloc);
+    const float m_new = fmaxf(m_run, mloc);
+    const float mb = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - mb);
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = fast_exp2(s[r] - mb);
+      psum += s[r];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    // O~^T += V^T P^T in 2-key chunks: chunk r pairs keys 8(r/4) + r%4 (lane
+    // group 0) and that + 4 (group 1), i.e. this lane's own register r.
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * C::VS + 32 * dt + l32], s[r], o[dt],
+                                                     0, 0, 0);
+      }
+  }
+
+  const float l_tot = pair_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  if (qrow < N) {
+    float *Orow = O + base + (size_t)qrow * D;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 v = {o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv, o[dt][4 * i + 2] * inv,
+                   o[dt][4 * i + 3] * inv};
+        *(f32x4 *)(Orow + 32 * dt + 8 * i + 4 * g) = v;
+      }
+    if (g == 0) LSE[(size_t)bh * N + qrow] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t fwd_b16(int BH, int N, const void *Q, const void *K, const void *V, float c2,
+                          void *O, float *LSE, hipStream_t st) {
+  using C = FwdCfg<D>;
+  const int nqb = (N + C::BR - 1) / C::BR;
+  const int total = nqb * BH;
+  hipLaunchKernelGGL((fwd_b16_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
+                     (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                     (uint16_t *)O, LSE, N, nqb, total, c2);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t fwd_f32(int BH, int N, const void *Q, const void *K, const void *V, float c2,
+                          void *O, float *LSE, hipStream_t st) {
+  using C = FwdF32Cfg<D>;
+  const int nqb = (N + C::BR - 1) / C::BR;
+  const int total = nqb * BH;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
+                     (const float *)Q, (const float *)K, (const float *)V, (float *)O, LSE, N,
+                     nqb, total, c2);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t fwd_b16_c(int causal, int BH, int N, const void *Q, const void *K,
+                            const void *V, float c2, void *O, float *LSE, hipStream_t st) {
+  return causal ? fwd_b16<T, D, true>(BH, N, Q, K, V, c2, O, LSE, st)
+                : fwd_b16<T, D, false>(BH, N, Q, K, V, c2, O, LSE, st);
+}
+
+hipError_t launch_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                      const void *V, float scale, int causal, void *O, float *LSE,
+                      hipStream_t st) {
+  const int BH = B * H;
+  const float c2 = scale * kLog2e;
+  if (dtype == kF32) {
+    if (d == 64)
+      return causal ? fwd_f32<64, true>(BH, N, Q, K, V, c2, O, LSE, st)
+                    : fwd_f32<64, false>(BH, N, Q, K, V, c2, O, LSE, st);
+    return causal ? fwd_f32<128, true>(BH, N, Q, K, V, c2, O, LSE, st)
+                  : fwd_f32<128, false>(BH, N, Q, K, V, c2, O, LSE, st);
+  }
+  if (dtype == kBF16)
+    return d == 64 ? fwd_b16_c<BF16, 64>(causal, BH, N, Q, K, V, c2, O, LSE, st)
+                   : fwd_b16_c<BF16, 128>(causal, BH, N, Q, K, V, c2, O, LSE, st);
+  return d == 64 ? fwd_b16_c<F16, 64>(causal, BH, N, Q, K, V, c2, O, LSE, st)
+                 : fwd_b16_c<F16, 128>(causal, BH, N, Q, K, V, c2, O, LSE, st);
+}
+
+}  // namespace fa

@@ -1,0 +1,162 @@
+/*
+ * fa.h -- C ABI of the exact-attention library for AMD MI355X (gfx950).
+ *
+ * Exact scaled-dot-product attention O = softmax(scale * Q K^T) V, computed
+ * tile by tile with the online-softmax rescaling so that no N x N matrix is
+ * ever written to device memory, and its gradient, which recomputes the
+ * scores and probabilities tile by tile from the saved per-row logsumexp.
+ *
+ * Sources (the pages this library follows):
+ *   [FA]  "Flash Attention" notes (sgdbs.github.io, AI_Infra / GPUKernel):
+ *         section 1 (overall structure: tiling, online softmax, recompute),
+ *         section 2 (online softmax; the two-block merge of (m, l) and of the
+ *         unnormalised output, parts 3 and 4, and the forward loop, part 4.2),
+ *         section 3 (recomputation: the saved statistic L = m + log l, part 3;
+ *         rebuilding P = exp(S - L), part 4.1; the blocked backward loop,
+ *         part 4.2), and the backward-derivation page (dV, dP, dS, dQ, dK in
+ *         parts 3-4; the identity rowsum(dP o P) = rowsum(dO o O), part 5;
+ *         the complete blocked backward, part 6).
+ *   [ASC] "FlashAttention backward: deleting the O(N^2) intermediates, how
+ *         can the gradient still be right?" (coreui.cn): the 1/sqrt(d_k)
+ *         factor carried into dQ and dK.
+ *
+ * Conventions shared by every entry point
+ *   dtype    FA_F32, FA_F16 or FA_BF16: element type of Q, K, V, O, dO, dQ,
+ *            dK and dV. LSE and every float workspace are fp32.
+ *   layout   Q, K, V, O, dO, dQ, dK, dV are dense [B, H, N, d] arrays, d
+ *            fastest (row n of slice (b, h) starts at ((b*H + h)*N + n)*d).
+ *            LSE and D are dense fp32 [B, H, N].
+ *   sizes    B >= 1, H >= 1, N >= 1, d in {64, 128}; B*H*N*d < 2^31.
+ *   causal   0: every query sees every key. 1: query i sees keys j <= i
+ *            (top-left aligned; queries and keys have the same length N).
+ *   scale    finite and > 0; the pages use 1/sqrt(d). S = scale * Q K^T.
+ *   pointers device pointers (hipMalloc'd or equivalent), 16-byte aligned,
+ *            owned by the caller. Outputs must not overlap inputs. The
+ *            library allocates, frees and synchronises nothing.
+ *   stream   a hipStream_t passed as void*; NULL means the null stream.
+ *            All work is enqueued on it and the call returns at once.
+ *   errors   Every entry point returns FA_OK (0) or a negative FA_ERR_*.
+ *            Arguments are checked before anything is enqueued; on an
+ *            argument error nothing is enqueued. FA_ERR_LAUNCH reports a
+ *            failed kernel launch (hipGetLastError after the launch); faults
+ *            inside a kernel surface at the caller's next synchronisation.
+ *            No C++ exception crosses this interface. The library keeps no
+ *            state between calls and may be called from several threads.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+/* element types */
+#define FA_F32 0
+#define FA_F16 1
+#define FA_BF16 2
+
+/* status codes */
+#define FA_OK 0
+#define FA_ERR_INVALID_ARG (-1) /* null or misaligned pointer, size <= 0,
+                                   scale not finite and > 0, causal not 0/1,
+                                   B*H*N*d too large */
+#define FA_ERR_UNSUPPORTED (-2) /* head size d or dtype not built */
+#define FA_ERR_WORKSPACE (-3)   /* workspace smaller than required */
+#define FA_ERR_LAUNCH (-4)      /* kernel launch failed */
+
+/* Version of this interface (FA_ABI_VERSION). */
+int fa_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char *fa_status_str(int status);
+
+/*
+ * Forward: O = softmax(scale * Q K^T) V per (batch, head) slice, and
+ * LSE_i = log sum_j exp(scale * q_i . k_j) (natural log, over the keys row i
+ * sees) -- [FA] section 2, part 4.2 (one pass over the key/value tiles with
+ * the (m, l, O~) rescaling, division by l deferred to the end) and section 3,
+ * part 3 (L = m + log l is the only statistic kept for the backward).
+ *
+ * In:  Q, K, V   [B, H, N, d] dtype
+ * Out: O         [B, H, N, d] dtype (rounded to nearest even once, at the end)
+ *      LSE       [B, H, N] fp32
+ * All dtypes are supported. For FA_F16/FA_BF16 the probabilities are rounded
+ * to dtype before the P V product; every sum is accumulated in fp32. For
+ * FA_F32 everything stays in fp32. Deterministic: the same inputs give
+ * bit-identical O and LSE.
+ */
+int fa_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+           const void *V, float scale, int causal, void *O, float *LSE,
+           void *stream);
+
+/*
+ * Bytes of workspace fa_bwd needs: fp32 D [B, H, N] followed (at a 256-byte
+ * aligned offset) by fp32 dQ accumulator [B, H, N, d]. Returns 0 for
+ * arguments fa_bwd would reject.
+ */
+size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d);
+
+/*
+ * Backward: given dO = dLoss/dO, the O and LSE that fa_fwd returned for the
+ * same Q, K, V, scale and causal, computes
+ *   D  = rowsum(dO o O)                        [FA] derivation page, part 5
+ *   P  = exp(scale * Q K^T - LSE)              [FA] section 3, part 4.1
+ *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D)
+ *   dQ = scale * dS K,  dK = scale * dS^T Q    [FA] derivation, parts 3-4;
+ *                                              [ASC] for the scale
+ * tile by tile, never forming an N x N array in device memory.
+ *
+ * In:  Q, K, V, O, dO  [B, H, N, d] dtype;  LSE [B, H, N] fp32
+ * Out: dQ, dK, dV      [B, H, N, d] dtype
+ * workspace: device memory of at least fa_bwd_workspace_bytes(...) bytes,
+ *   256-byte aligned, owned by the caller; overwritten (no need to clear it).
+ * dtype: FA_F16 and FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED). P and dS
+ * are rounded to dtype before the products that consume them; all sums are
+ * fp32. dK and dV are deterministic; dQ is summed with fp32 atomics and may
+ * differ in the last bits between runs.
+ * Enqueues, in order: fa_bwd_preprocess, fa_bwd_main, fa_bwd_dq_convert.
+ */
+int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+           const void *V, const void *O, const void *dO, const float *LSE,
+           float scale, int causal, void *dQ, void *dK, void *dV,
+           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The three stages of fa_bwd, for callers that schedule them separately.
+ *
+ * fa_bwd_preprocess: Dvec_i = sum_k dO_ik * O_ik in fp32 ([FA] derivation
+ *   page, part 5: computed once before the blocked loop, part 6) and
+ *   dQacc = 0.  In: O, dO [B,H,N,d] dtype.  Out: Dvec [B,H,N] fp32,
+ *   dQacc [B,H,N,d] fp32 (both caller-owned).
+ */
+int fa_bwd_preprocess(int dtype, int B, int H, int N, int d, const void *O,
+                      const void *dO, float *Dvec, float *dQacc, void *stream);
+
+/*
+ * fa_bwd_main: the blocked backward loop ([FA] section 3, part 4.2 and the
+ *   derivation page, part 6) with the loops swapped: one workgroup owns a
+ *   block of keys, keeps its dK and dV in registers, and walks the query
+ *   tiles; dQ contributions (without the scale) are added atomically into
+ *   dQacc, which must hold zeros (or a partial sum) on entry.
+ *   In: Q, K, V, dO dtype; LSE, Dvec fp32.  Out: dK, dV dtype; dQacc fp32 +=.
+ */
+int fa_bwd_main(int dtype, int B, int H, int N, int d, const void *Q,
+                const void *K, const void *V, const void *dO, const float *LSE,
+                const float *Dvec, float scale, int causal, float *dQacc,
+                void *dK, void *dV, void *stream);
+
+/*
+ * fa_bwd_dq_convert: dQ = dtype(scale * dQacc), rounded to nearest even.
+ */
+int fa_bwd_dq_convert(int dtype, int B, int H, int N, int d,
+                      const float *dQacc, float scale, void *dQ, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/fa.h declares, and rejects bad arguments before enqueuing anything.
+
+Only argument-error paths are called here: they return before any HIP call,
+so they run on a machine without a GPU."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import exact_attention_34_amd as fa
+    if not os.path.exists(fa.library_path()):
+        from exact_attention_34_amd import build
+        build.build()
+    return fa.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def _status(name):
+    text = open(HEADER).read()
+    return int(re.search(r"#define\s+%s\s+\(?(-?\d+)\)?" % name, text).group(1))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert "fa_fwd" in names and "fa_bwd" in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.fa_abi_version() == _status("FA_ABI_VERSION")
+    for code in (0, -1, -2, -3, -4):
+        s = L.fa_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert L.fa_status_str(7).decode() == "unknown status"
+
+
+# Fake, 16-byte-aligned "device" addresses: never dereferenced, because every
+# call below fails its argument checks first.
+A = ctypes.c_void_p(0x10000)
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)
+NUL = ctypes.c_void_p(0)
+
+INVALID = _status("FA_ERR_INVALID_ARG")
+UNSUP = _status("FA_ERR_UNSUPPORTED")
+WS = _status("FA_ERR_WORKSPACE")
+
+
+def fwd(L, dtype=2, B=1, H=1, N=16, d=64, q=A, k=A, v=A, scale=0.125, causal=0, o=A2,
+        lse=A2):
+    return L.fa_fwd(dtype, B, H, N, d, q, k, v, scale, causal, o, lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID),
+    (dict(d=0), INVALID), (dict(d=96), UNSUP), (dict(d=256), UNSUP),
+    (dict(dtype=3), UNSUP), (dict(dtype=-1), UNSUP),
+    (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(scale=math.nan), INVALID), (dict(scale=math.inf), INVALID),
+    (dict(causal=2), INVALID), (dict(causal=-1), INVALID),
+    (dict(q=NUL), INVALID), (dict(k=NUL), INVALID), (dict(v=NUL), INVALID),
+    (dict(o=NUL), INVALID), (dict(lse=NUL), INVALID),
+    (dict(q=MIS), INVALID), (dict(o=MIS), INVALID),
+    (dict(B=1 << 12, H=1 << 12, N=1 << 10, d=128), INVALID),  # > 2^31 elements
+])
+def test_fwd_rejects(L, kw, code):
+    assert fwd(L, **kw) == code
+
+
+def _bwd(L, dtype=2, N=16, d=64, ws=A, ws_bytes=None, causal=0, scale=0.125, dq=A2, lse=A2):
+    if ws_bytes is None:
+        ws_bytes = L.fa_bwd_workspace_bytes(dtype, 1, 1, N, d)
+    return L.fa_bwd(dtype, 1, 1, N, d, A, A, A, A, A, lse, scale, causal, dq, A2, A2, ws,
+                    ws_bytes, None)
+
+
+def test_bwd_rejects(L):
+    assert _bwd(L, dtype=0) == UNSUP          # fp32 backward is not built
+    assert _bwd(L, d=32) == UNSUP
+    assert _bwd(L, N=-3) == INVALID
+    assert _bwd(L, scale=math.nan) == INVALID
+    assert _bwd(L, causal=5) == INVALID
+    assert _bwd(L, ws=NUL) == INVALID
+    assert _bwd(L, dq=MIS) == INVALID
+    assert _bwd(L, lse=NUL) == INVALID
+    need = L.fa_bwd_workspace_bytes(2, 1, 1, 16, 64)
+    assert _bwd(L, ws_bytes=need - 1) == WS
+
+
+def test_stage_entry_points_reject(L):
+    assert L.fa_bwd_preprocess(2, 1, 1, 0, 64, A, A, A, A, None) == INVALID
+    assert L.fa_bwd_preprocess(2, 1, 1, 8, 64, A, NUL, A, A, None) == INVALID
+    assert L.fa_bwd_main(1, 1, 1, 8, 64, A, A, A, A, A, A, 0.1, 3, A, A, A, None) == INVALID
+    assert L.fa_bwd_main(0, 1, 1, 8, 64, A, A, A, A, A, A, 0.1, 0, A, A, A, None) == UNSUP
+    assert L.fa_bwd_dq_convert(2, 1, 1, 8, 64, A, -0.5, A, None) == INVALID
+    assert L.fa_bwd_dq_convert(2, 1, 1, 8, 64, MIS, 0.5, A, None) == INVALID
+
+
+@pytest.mark.parametrize("dtype,B,H,N,d", [(2, 1, 1, 1, 64), (1, 2, 3, 1000, 128),
+                                          (2, 16, 32, 2048, 128)])
+def test_workspace_bytes(L, dtype, B, H, N, d):
+    """fp32 D [B,H,N] rounded up to 256 bytes, then fp32 dQ [B,H,N,d]."""
+    dbytes = -(-B * H * N * 4 // 256) * 256
+    assert L.fa_bwd_workspace_bytes(dtype, B, H, N, d) == dbytes + B * H * N * d * 4
+    assert L.fa_bwd_workspace_bytes(0, B, H, N, d) == 0     # fp32: no backward
+    assert L.fa_bwd_workspace_bytes(dtype, B, H, N, 80) == 0
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    """The Python face rejects CPU tensors instead of computing anything."""
+    import torch
+    import exact_attention_34_amd as fa
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q)
