@@ -158,7 +158,7 @@ def slice_errors(outs, b, h, o_ref, lse_ref, g):
             "dv_rel_l2": rel(a(outs["dv"]), g["dv"])}
 
 
-def cpu_baseline(w, host, outs, min_seconds=10.0, max_slices=8):
+def cpu_baseline(w, host, outs, min_seconds=10.0, max_slices=256):
     """The fp64 oracle on whole (batch, head) slices of the same workload,
     until min_seconds of work; also compares those slices with the GPU run."""
     import oracle
@@ -191,17 +191,31 @@ def main():
     ap.add_argument("--workload", default="c5")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (scales the HBM "
+                         "byte counters read under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the path has no multi-GPU mode "
-              "(each (batch, head) slice is independent; see the sharding notes). "
-              "Run with --gpus 1.", file=sys.stderr, flush=True)
+        print("bench.py measures one GPU only: this library has no multi-GPU path. "
+              "(Every (batch, head) slice is independent, so several GPUs would each "
+              "run the one-GPU kernels on their share of slices.) Run with --gpus 1.",
+              file=sys.stderr, flush=True)
         sys.exit(2)
 
     import torch
     import attn_inputs as ai
     import exact_attention_34_amd as fa
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "dispatches": 5}), flush=True)
+        return
     fa.lib()
 
     w = ai.WORKLOADS[args.workload]

@@ -18,8 +18,9 @@
 // dP = dO V^T. S/P and dP/dS come out of the MFMA with one key per lane
 // (column l % 32) and 16 query rows per lane, which is exactly the B-operand
 // layout of dV^T = dO^T P and dK^T = Q^T dS, so P and dS never leave
-// registers for those two products; dO^T and Q^T come from LDS copies stored
-// transposed with the query index in swap23 order. dS is also written to LDS,
+// registers for those two products; the dO^T and Q^T operands are read from
+// the row-major tiles with transposing LDS reads (ds_read_b64_tr_b16). dS is
+// also written to LDS,
 // where each wave reads a 32x32 (query, column) tile of dQ = dS K over all KB
 // keys and adds it into the fp32 workspace.
 
@@ -90,20 +91,17 @@ struct BwdCfg {
   static constexpr int NCH = D / 16;
   static constexpr int NDT = D / 32;
   static constexpr int TPR = D / 8;
-  static constexpr int QS = D + 8;   // row-major Q / dO stride
-  static constexpr int TS = BR + 8;  // transposed Q^T / dO^T stride
+  static constexpr int QS = D + 32;  // Q / dO row stride: an odd multiple of 64 bytes (swizzled)
   static constexpr int SS = KB + 8;  // dS row stride
   static constexpr int KSTG = D + 8; // K staging stride (prologue only)
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_DO = OFF_Q + BR * QS;
-  static constexpr int OFF_QT = OFF_DO + BR * QS;
-  static constexpr int OFF_DOT = OFF_QT + D * TS;
-  static constexpr int OFF_DS = OFF_DOT + D * TS;
-  static constexpr int N16 = OFF_DS + BR * SS;       // 16-bit elements
+  static constexpr int OFF_DS = OFF_DO + BR * QS;
+  static constexpr int N16_LOOP = OFF_DS + BR * SS;
+  static constexpr int N16 = (N16_LOOP > KB * KSTG) ? N16_LOOP : KB * KSTG;  // 16-bit elements
   static constexpr int CPT = (BR * D / 8) / kThreads;  // 16-byte chunks per thread per tensor
-  static_assert(CPT == 2, "each thread loads a pair of rows");
+  static_assert(CPT == 2, "each thread loads two chunks per tensor");
   static_assert(NQT * NDT == 4, "one 32x32 dQ tile per wave");
-  static_assert(KB * KSTG <= N16, "K staging fits");
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -117,8 +115,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::N16];
   __shared__ float lse2s[C::BR];
   __shared__ float dvs[C::BR];
-  uint16_t *Qs = lds + C::OFF_Q, *dOs = lds + C::OFF_DO;
-  uint16_t *QT = lds + C::OFF_QT, *dOT = lds + C::OFF_DOT, *dSs = lds + C::OFF_DS;
+  uint16_t *Qs = lds + C::OFF_Q, *dOs = lds + C::OFF_DO, *dSs = lds + C::OFF_DS;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -165,17 +162,18 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   const int nq = (N + C::BR - 1) / C::BR;
   const int it0 = CAUSAL ? k0 / C::BR : 0;  // earlier queries see none of these keys
 
-  // Query-tile prefetch: each thread loads rows 2*rp, 2*rp+1 at columns d0..d0+7.
-  const int rp = tid / C::TPR, d0 = 8 * (tid % C::TPR);
+  // Query-tile prefetch: chunk c = tid + 256*r of the tile is row c / TPR,
+  // 16-byte chunk c % TPR; stored row-major with the chunk swizzle.
   u32x4 qpre[2], dopre[2];
   float lpre = 0.f, dpre = 0.f;
   auto gload = [&](int it) {
     const int q0 = it * C::BR;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int q = q0 + 2 * rp + r;
-      qpre[r] = (q < N) ? ld128(Qh + (size_t)q * D + d0) : zero4;
-      dopre[r] = (q < N) ? ld128(dOh + (size_t)q * D + d0) : zero4;
+      const int c = tid + C::kThreads * r;
+      const int q = q0 + c / C::TPR, col = 8 * (c % C::TPR);
+      qpre[r] = (q < N) ? ld128(Qh + (size_t)q * D + col) : zero4;
+      dopre[r] = (q < N) ? ld128(dOh + (size_t)q * D + col) : zero4;
     }
     if (tid < C::BR) {
       const int q = q0 + tid;
@@ -186,22 +184,30 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   auto swrite = [&]() {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      st128(Qs + (2 * rp + r) * C::QS + d0, qpre[r]);
-      st128(dOs + (2 * rp + r) * C::QS + d0, dopre[r]);
-    }
-    const int p = swap23(2 * rp);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int h = e >> 1;
-      *(uint32_t *)(QT + (d0 + e) * C::TS + p) =
-          (e & 1) ? pair_hi(qpre[0][h], qpre[1][h]) : pair_lo(qpre[0][h], qpre[1][h]);
-      *(uint32_t *)(dOT + (d0 + e) * C::TS + p) =
-          (e & 1) ? pair_hi(dopre[0][h], dopre[1][h]) : pair_lo(dopre[0][h], dopre[1][h]);
+      const int c = tid + C::kThreads * r;
+      const int row = c / C::TPR, pos = 8 * swz(row, c % C::TPR);
+      st128(Qs + row * C::QS + pos, qpre[r]);
+      st128(dOs + row * C::QS + pos, dopre[r]);
     }
     if (tid < C::BR) {
       lse2s[tid] = lpre;
       dvs[tid] = dpre;
     }
+  };
+  // Row-wise operand read (lane = row, 8 consecutive columns 16c + 8g).
+  auto rd_row = [&](const uint16_t *tile, int row, int c) {
+    return ld128(tile + row * C::QS + 8 * swz(row, 2 * c + g));
+  };
+  // Transposed operand read: rows q0 + 4g + (l%16)/4 and that + 8, column
+  // block 32dt + 16*((l/16)%2) + 4*(l%4) -> lane holds column 32dt + l%32 at
+  // rows q0 + 4g + (0..3) and q0 + 8 + 4g + (0..3).
+  const int tr_row = 4 * g + (lane & 15) / 4;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto rd_tr = [&](const uint16_t *tile, int q0, int dt) {
+    const int r1 = q0 + tr_row, r2 = r1 + 8, col = 32 * dt + tr_col;
+    const u32x2 a = ld_tr16(tile + r1 * C::QS + 8 * swz(r1, col >> 3) + (col & 7));
+    const u32x2 b = ld_tr16(tile + r2 * C::QS + 8 * swz(r2, col >> 3) + (col & 7));
+    return cat(a, b);
   };
 
   // dK^T and dV^T accumulators: column = key (l % 32), rows = d.
@@ -233,15 +239,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
         dp[qt][r] = 0.f;
       }
 #pragma unroll
-      for (int c = 0; c < C::NCH; ++c) {
-        const u32x4 a = ld128(Qs + (32 * qt + l32) * C::QS + 16 * c + 8 * g);
-        s[qt] = mfma32<T>(a, kreg[c], s[qt]);
-      }
+      for (int c = 0; c < C::NCH; ++c)
+        s[qt] = mfma32<T>(rd_row(Qs, 32 * qt + l32, c), kreg[c], s[qt]);
 #pragma unroll
-      for (int c = 0; c < C::NCH; ++c) {
-        const u32x4 a = ld128(dOs + (32 * qt + l32) * C::QS + 16 * c + 8 * g);
-        dp[qt] = mfma32<T>(a, vreg[c], dp[qt]);
-      }
+      for (int c = 0; c < C::NCH; ++c)
+        dp[qt] = mfma32<T>(rd_row(dOs, 32 * qt + l32, c), vreg[c], dp[qt]);
     }
 #pragma unroll
     for (int qt = 0; qt < C::NQT; ++qt)
@@ -266,10 +268,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 #pragma unroll
       for (int qt = 0; qt < C::NQT; ++qt)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const u32x4 a = ld128(dOT + (32 * dt + l32) * C::TS + 32 * qt + 16 * cc + 8 * g);
-          dv[dt] = mfma32<T>(a, pk[qt][cc], dv[dt]);
-        }
+        for (int cc = 0; cc < 2; ++cc)
+          dv[dt] = mfma32<T>(rd_tr(dOs, 32 * qt + 16 * cc, dt), pk[qt][cc], dv[dt]);
     // dS = P o (dP - D)
 #pragma unroll
     for (int qt = 0; qt < C::NQT; ++qt)
@@ -291,10 +291,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 #pragma unroll
       for (int qt = 0; qt < C::NQT; ++qt)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const u32x4 a = ld128(QT + (32 * dt + l32) * C::TS + 32 * qt + 16 * cc + 8 * g);
-          dk[dt] = mfma32<T>(a, pk[qt][cc], dk[dt]);
-        }
+        for (int cc = 0; cc < 2; ++cc)
+          dk[dt] = mfma32<T>(rd_tr(Qs, 32 * qt + 16 * cc, dt), pk[qt][cc], dk[dt]);
     // dS (16-bit) to LDS, [query][key]
 #pragma unroll
     for (int qt = 0; qt < C::NQT; ++qt)

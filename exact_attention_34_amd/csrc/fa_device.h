@@ -113,4 +113,30 @@ __device__ __forceinline__ int xcd_tile(int wg, int total) {
 __device__ __forceinline__ u32x4 ld128(const void *p) { return *(const u32x4 *)p; }
 __device__ __forceinline__ void st128(void *p, const u32x4 &v) { *(u32x4 *)p = v; }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i % 4) of the 8-byte words that source lanes i/4, 4 + i/4, 8 + i/4 and
+// 12 + i/4 address. If source lane r points at row k0 + r/4, columns
+// c0 + 4*(r%4) .. +3 of a row-major 16-bit tile, lane i receives rows
+// k0..k0+3 of column c0 + i: four consecutive k values of one column, i.e.
+// half of an MFMA operand whose contraction index runs along the tile's rows.
+__device__ __forceinline__ u32x2 ld_tr16(const uint16_t *p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// 16-byte-chunk swizzle for a row-major tile with a row stride of an odd
+// multiple of 64 bytes. LDS has 64 banks of 4 bytes. Transposing reads
+// (4 consecutive rows x 64 bytes per half-wave) are conflict-free with that
+// stride; XOR-ing the chunk index with (row / 4) % 4 also spreads the rows of
+// a 16-lane group of row-wise 16-byte reads over all 64 banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+__device__ __forceinline__ u32x4 cat(const u32x2 &a, const u32x2 &b) {
+  u32x4 r = {a[0], a[1], b[0], b[1]};
+  return r;
+}
+
 }  // namespace fa

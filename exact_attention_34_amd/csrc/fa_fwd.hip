@@ -19,8 +19,9 @@
 //   * Row max and row sum are in-register reductions plus one
 //     v_permlane32_swap between the wave halves.
 //   * P, rounded to the input type, is the B operand of O~^T += V^T P^T
-//     straight from registers; V^T comes from LDS.
-//   * K (row-major) and V^T tiles are double-buffered in LDS: the global
+//     straight from registers; the V^T operand is read from the row-major V
+//     tile with transposing LDS reads (ds_read_b64_tr_b16).
+//   * K and V tiles are double-buffered in LDS, row-major: the global
 //     loads of tile j+1 are issued before the MFMAs of tile j and written to
 //     the other buffer after them, one barrier per tile.
 // The fp32 variant is the same loop on v_mfma_f32_32x32x2_f32 with P kept in
@@ -37,14 +38,13 @@ struct FwdCfg {
   static constexpr int BR = 128;        // query rows per workgroup, 32 per wave
   static constexpr int BC = 64;         // keys per tile
   static constexpr int KS = D + 8;      // K tile row stride (16-bit elements)
-  static constexpr int VS = BC + 8;     // V^T tile row stride
+  static constexpr int VS = D + 32;     // V tile row stride: an odd multiple of 64 bytes
   static constexpr int KTILE = BC * KS;
-  static constexpr int VTILE = D * VS;
+  static constexpr int VTILE = BC * VS;
   static constexpr int NCH = D / 16;    // 16-wide k chunks of q . k
   static constexpr int NDT = D / 32;    // 32-wide output column tiles
   static constexpr int TPR = D / 8;     // threads per row in a 16-byte-chunk load
   static constexpr int KCH = (BC * D / 8) / kThreads;  // 16-byte chunks per thread per tile
-  static_assert(KCH == 2 || KCH == 4, "tile split");
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -78,8 +78,6 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
 
   // Global -> register prefetch of one K/V tile.
   u32x4 kpre[C::KCH], vpre[C::KCH];
-  const int vk0 = C::KCH * (tid / C::TPR);  // first of this thread's V keys
-  const int vd0 = 8 * (tid % C::TPR);       // first of its 8 columns
   auto gload = [&](int kt) {
     const int kb = kt * C::BC;
 #pragma unroll
@@ -87,38 +85,23 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
       const int c = tid + C::kThreads * r;
       const int key = kb + c / C::TPR, col = 8 * (c % C::TPR);
       kpre[r] = (key < N) ? ld128(Kh + (size_t)key * D + col) : zero4;
-    }
-#pragma unroll
-    for (int r = 0; r < C::KCH; ++r) {
-      const int key = kb + vk0 + r;
-      vpre[r] = (key < N) ? ld128(Vh + (size_t)key * D + vd0) : zero4;
+      vpre[r] = (key < N) ? ld128(Vh + (size_t)key * D + col) : zero4;
     }
   };
-  // Register -> LDS: K row-major, V transposed with keys in swap23 order.
+  // Register -> LDS, both tiles row-major.
   auto swrite = [&](int buf) {
     uint16_t *Ks = lds + buf * (C::KTILE + C::VTILE);
-    uint16_t *Vt = Ks + C::KTILE;
+    uint16_t *Vs = Ks + C::KTILE;
 #pragma unroll
     for (int r = 0; r < C::KCH; ++r) {
       const int c = tid + C::kThreads * r;
       st128(Ks + (c / C::TPR) * C::KS + 8 * (c % C::TPR), kpre[r]);
-    }
-    const int p0 = swap23(vk0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int h = e >> 1;
-      uint16_t *dst = Vt + (vd0 + e) * C::VS + p0;
-      if constexpr (C::KCH == 4) {
-        u32x2 v;
-        v[0] = (e & 1) ? pair_hi(vpre[0][h], vpre[1][h]) : pair_lo(vpre[0][h], vpre[1][h]);
-        v[1] = (e & 1) ? pair_hi(vpre[2][h], vpre[3][h]) : pair_lo(vpre[2][h], vpre[3][h]);
-        *(u32x2 *)dst = v;
-      } else {
-        *(uint32_t *)dst =
-            (e & 1) ? pair_hi(vpre[0][h], vpre[1][h]) : pair_lo(vpre[0][h], vpre[1][h]);
-      }
+      st128(Vs + (c / C::TPR) * C::VS + 8 * (c % C::TPR), vpre[r]);
     }
   };
+  // Source address of this lane's transposing reads of V: rows 4*g + (l%16)/4
+  // (+ 8 for the second half of the operand), columns 16*((l/16)%2) + 4*(l%4).
+  const int tr_off = (4 * g + (lane & 15) / 4) * C::VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 o[C::NDT];
 #pragma unroll
@@ -135,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
     if (kt + 1 < ntiles) gload(kt + 1);
     __syncthreads();
     const uint16_t *Ks = lds + buf * (C::KTILE + C::VTILE);
-    const uint16_t *Vt = Ks + C::KTILE;
+    const uint16_t *Vs = Ks + C::KTILE;
     const int kb = kt * C::BC;
     // Under the causal mask a wave whose rows all precede the tile skips it.
     if (!CAUSAL || kb <= wq0 + 31) {
@@ -187,7 +170,10 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
       }
-      // P as B operand: 16-key chunk cc of subtile t = registers 8cc..8cc+7.
+      // P as B operand: 16-key chunk cc of subtile t = registers 8cc..8cc+7,
+      // i.e. keys 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3); the A operand
+      // V^T takes the same keys for column 32dt + l%32 with two transposing
+      // reads.
       u32x4 pp[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -202,7 +188,8 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            const u32x4 a = ld128(Vt + (32 * dt + l32) * C::VS + 32 * t + 16 * cc + 8 * g);
+            const uint16_t *src = Vs + tr_off + (32 * t + 16 * cc) * C::VS + 32 * dt;
+            const u32x4 a = cat(ld_tr16(src), ld_tr16(src + 8 * C::VS));
             o[dt] = mfma32<T>(a, pp[t][cc], o[dt]);
           }
     }
