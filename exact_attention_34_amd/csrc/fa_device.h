@@ -134,6 +134,41 @@ __device__ __forceinline__ u32x2 ld_tr16(const uint16_t *p) {
 // a 16-lane group of row-wise 16-byte reads over all 64 banks.
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
+// Direct 16-byte global -> LDS load (global_load_lds_dwordx4): every lane
+// reads 16 bytes at its own global address; the wave writes them to 1 KiB of
+// LDS starting at lds_base (wave-uniform), lane l at lds_base + 16 l. The
+// write is tracked by the vector-memory counter.
+__device__ __forceinline__ void load_lds16(const void *gptr, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16,
+                                   0, 0);
+}
+// Buffer resource for raw (unformatted) buffer access on gfx9: 48-bit base,
+// stride 0, size in bytes (accesses at or past it read as zero), word 3 as
+// the gfx9 raw-buffer format.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+__device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void *lds,
+                                    int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// Direct 16-byte buffer -> LDS load (buffer_load_dwordx4 ... lds): lane l
+// reads 16 bytes at byte offset voffset + soffset of the buffer and the wave
+// writes them to LDS at lds_base + 16 l (lds_base wave-uniform).
+__device__ __forceinline__ void buffer_load_lds16(const i32x4 &rsrc, int voffset, int soffset,
+                                                  void *lds_base) {
+  raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_base, 16, voffset,
+                      soffset, 0, 0);
+}
+// Wait until every vector-memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ u32x4 cat(const u32x2 &a, const u32x2 &b) {
   u32x4 r = {a[0], a[1], b[0], b[1]};
   return r;

@@ -21,11 +21,14 @@
 //   * P, rounded to the input type, is the B operand of O~^T += V^T P^T
 //     straight from registers; the V^T operand is read from the row-major V
 //     tile with transposing LDS reads (ds_read_b64_tr_b16).
-//   * K and V tiles are double-buffered in LDS, row-major: the global
-//     loads of tile j+1 are issued before the MFMAs of tile j and written to
-//     the other buffer after them, one barrier per tile.
+//   * K and V tiles are double-buffered in LDS (row-major, XOR-swizzled at
+//     16-byte granularity) and filled by direct global->LDS loads
+//     (global_load_lds_dwordx4): the loads of tile j+1 are issued right after
+//     the barrier that opens tile j and land while tile j is computed.
 // The fp32 variant is the same loop on v_mfma_f32_32x32x2_f32 with P kept in
 // fp32.
+
+#include <type_traits>
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -34,18 +37,33 @@ namespace fa {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int kThreads = 256;  // 4 waves
-  static constexpr int BR = 128;        // query rows per workgroup, 32 per wave
-  static constexpr int BC = 64;         // keys per tile
-  static constexpr int KS = D + 8;      // K tile row stride (16-bit elements)
-  static constexpr int VS = D + 32;     // V tile row stride: an odd multiple of 64 bytes
-  static constexpr int KTILE = BC * KS;
-  static constexpr int VTILE = BC * VS;
-  static constexpr int NCH = D / 16;    // 16-wide k chunks of q . k
-  static constexpr int NDT = D / 32;    // 32-wide output column tiles
-  static constexpr int TPR = D / 8;     // threads per row in a 16-byte-chunk load
-  static constexpr int KCH = (BC * D / 8) / kThreads;  // 16-byte chunks per thread per tile
+  static constexpr int kThreads = 256;       // 4 waves
+  static constexpr int BR = 128;             // query rows per workgroup, 32 per wave
+  static constexpr int BC = 64;              // keys per tile
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int TILE = BC * D;        // 16-bit elements per K or V tile
+  static constexpr int NCH = D / 16;         // 16-wide k chunks of q . k
+  static constexpr int NDT = D / 32;         // 32-wide output column tiles
+  static constexpr int LPW = BC * CPR / 256; // direct loads per wave per tile and tensor
+  static constexpr int SH = (CPR == 16) ? 0 : 1;
 };
+
+// LDS tiles are unpadded and row-major at 16-byte-chunk granularity, with the
+// chunk index of row r XOR-ed by a row function (64 banks of 4 bytes):
+//  * K, read row-wise (16 consecutive rows, one chunk each, per quarter-wave):
+//    swz_k spreads 16 consecutive rows over the 16 four-bank groups;
+//  * V, read with transposing loads (4 consecutive rows x 4 chunks per
+//    half-wave): swz_v makes those 16 chunks land in distinct bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  using C = FwdCfg<D>;
+  return (row >> C::SH) & (C::CPR - 1);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  using C = FwdCfg<D>;
+  return (4 * (row >> C::SH)) & (C::CPR - 4);
+}
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
@@ -53,7 +71,10 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int N,
     int nqb, int total, float c2) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (C::KTILE + C::VTILE)];
+  // Two buffers per tensor, named separately so that the compiler sees that
+  // the direct loads into one never alias the reads of the other.
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[C::TILE], V0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t K1[C::TILE], V1[C::TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -67,41 +88,66 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
   const size_t base = (size_t)bh * N * D;
   const uint16_t *Qh = Q + base, *Kh = K + base, *Vh = V + base;
 
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  // Rows and keys past N are read from row N - 1 (clamped, always valid
+  // memory): their queries are never stored and their keys are masked.
   u32x4 qreg[C::NCH];
+  const int qld = min(qrow, N - 1);
 #pragma unroll
-  for (int c = 0; c < C::NCH; ++c)
-    qreg[c] = (qrow < N) ? ld128(Qh + (size_t)qrow * D + 16 * c + 8 * g) : zero4;
+  for (int c = 0; c < C::NCH; ++c) qreg[c] = ld128(Qh + (size_t)qld * D + 16 * c + 8 * g);
 
   const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
   const int ntiles = (kend + C::BC - 1) / C::BC;
 
-  // Global -> register prefetch of one K/V tile.
-  u32x4 kpre[C::KCH], vpre[C::KCH];
-  auto gload = [&](int kt) {
+  // Direct buffer -> LDS loads: instruction i of wave w fills LDS chunks
+  // (w*LPW + i)*64 + lane; this lane fetches the global chunk that belongs
+  // there under the swizzle. Offsets are bytes within the (b, h) slice.
+  const i32x4 krs = make_rsrc(Kh, (uint32_t)N * D * 2);
+  const i32x4 vrs = make_rsrc(Vh, (uint32_t)N * D * 2);
+  int gk[C::LPW], gv[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int p = (w * C::LPW + i) * 64 + lane;
+    const int r = p / C::CPR, sw = p % C::CPR;
+    gk[i] = 2 * (r * D + 8 * (sw ^ swz_k<D>(r)));
+    gv[i] = 2 * (r * D + 8 * (sw ^ swz_v<D>(r)));
+  }
+  auto issue = [&](uint16_t *Kb, uint16_t *Vb, int kt) __attribute__((always_inline)) {
     const int kb = kt * C::BC;
+    const int soff = kb * D * 2;
+    if (kb + C::BC <= N) {
 #pragma unroll
-    for (int r = 0; r < C::KCH; ++r) {
-      const int c = tid + C::kThreads * r;
-      const int key = kb + c / C::TPR, col = 8 * (c % C::TPR);
-      kpre[r] = (key < N) ? ld128(Kh + (size_t)key * D + col) : zero4;
-      vpre[r] = (key < N) ? ld128(Vh + (size_t)key * D + col) : zero4;
+      for (int i = 0; i < C::LPW; ++i) {
+        buffer_load_lds16(krs, gk[i], soff, Kb + (w * C::LPW + i) * 512);
+        buffer_load_lds16(vrs, gv[i], soff, Vb + (w * C::LPW + i) * 512);
+      }
+    } else {
+      // Tail tile: rows past N re-read row N - 1 (their keys are masked).
+#pragma unroll
+      for (int i = 0; i < C::LPW; ++i) {
+        const int r = ((w * C::LPW + i) * 64 + lane) / C::CPR;
+        const int shift = 2 * D * (min(kb + r, N - 1) - kb - r);  // <= 0
+        buffer_load_lds16(krs, gk[i] + shift, soff, Kb + (w * C::LPW + i) * 512);
+        buffer_load_lds16(vrs, gv[i] + shift, soff, Vb + (w * C::LPW + i) * 512);
+      }
     }
   };
-  // Register -> LDS, both tiles row-major.
-  auto swrite = [&](int buf) {
-    uint16_t *Ks = lds + buf * (C::KTILE + C::VTILE);
-    uint16_t *Vs = Ks + C::KTILE;
+
+  // Per-lane operand offsets (elements). K, row-wise: row 32t + l%32,
+  // chunk 2c + g. V, transposing: rows 4g + (l%16)/4 (+8 for the upper half
+  // of the operand) of each 16-key chunk, columns 32dt + 16((l/16)%2) +
+  // 4(l%4); the swizzle term depends on the lane only.
+  int koff[C::NCH], voff[C::NDT];
+  {
+    const int kx = swz_k<D>(l32);
 #pragma unroll
-    for (int r = 0; r < C::KCH; ++r) {
-      const int c = tid + C::kThreads * r;
-      st128(Ks + (c / C::TPR) * C::KS + 8 * (c % C::TPR), kpre[r]);
-      st128(Vs + (c / C::TPR) * C::VS + 8 * (c % C::TPR), vpre[r]);
-    }
-  };
-  // Source address of this lane's transposing reads of V: rows 4*g + (l%16)/4
-  // (+ 8 for the second half of the operand), columns 16*((l/16)%2) + 4*(l%4).
-  const int tr_off = (4 * g + (lane & 15) / 4) * C::VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    for (int c = 0; c < C::NCH; ++c) koff[c] = l32 * D + 8 * ((2 * c + g) ^ kx);
+    const int vr = 4 * g + (lane & 15) / 4;
+    const int vx = swz_v<D>(vr);
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+      voff[dt] = vr * D + 8 * ((4 * dt + 2 * ((lane >> 4) & 1) + (lane & 3) / 2) ^ vx) +
+                 4 * (lane & 1);
+  }
 
   f32x16 o[C::NDT];
 #pragma unroll
@@ -111,89 +157,119 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
   float m_run = -INFINITY;  // running max of scaled scores (base-2 units)
   float l_run = 0.f;        // this lane's share of the running normaliser
 
-  gload(0);
-  swrite(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
-    __syncthreads();
-    const uint16_t *Ks = lds + buf * (C::KTILE + C::VTILE);
-    const uint16_t *Vs = Ks + C::KTILE;
-    const int kb = kt * C::BC;
-    // Under the causal mask a wave whose rows all precede the tile skips it.
-    if (!CAUSAL || kb <= wq0 + 31) {
-      f32x16 s[2];
+  // One K/V tile. MASK selects the variant for tiles that hold keys past N or
+  // past this wave's first query row (causal); other tiles skip the mask.
+  auto step = [&](const uint16_t *Ks, const uint16_t *Vs, int kb,
+                  auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // Phase boundaries below are scheduling barriers: within a phase the
+    // compiler interleaves freely, across them it may not hoist operand
+    // reads (which would exceed the register budget of two waves per SIMD).
+    __builtin_amdgcn_sched_barrier(0);
+    // S^T = K Q^T, two 32-key subtiles; lane: query qrow, keys 8(r/4)+4g+r%4.
+    f32x16 s[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
 #pragma unroll
-        for (int c = 0; c < C::NCH; ++c) {
-          const u32x4 a = ld128(Ks + (32 * t + l32) * C::KS + 16 * c + 8 * g);
-          s[t] = mfma32<T>(a, qreg[c], s[t]);
+    for (int c = 0; c < C::NCH; ++c)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        s[t] = mfma32<T>(ld128(Ks + koff[c] + 32 * t * D), qreg[c], s[t]);
+    // Pipeline the operand reads two MFMA pairs ahead of their use.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < C::NCH - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // Row max of the raw scores (scale > 0 commutes with max).
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (MASK) {
+          const int key = kb + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= N || (CAUSAL && key > qrow)) s[t][r] = -INFINITY;
         }
+        mloc = fmaxf(mloc, s[t][r]);
       }
-      // scale to base 2, mask, tile row max
-      const bool need_mask = (kb + C::BC > N) || (CAUSAL && kb + C::BC - 1 > wq0);
-      float mloc = -INFINITY;
+    mloc = pair_max(mloc);
+    const float m_new = fmaxf(m_run, mloc * c2);
+    const float mb = (m_new == -INFINITY) ? 0.f : m_new;  // never form -inf - -inf
+    const float alpha = fast_exp2(m_run - mb);
+    // P = 2^(s*c2 - m); one FMA and one exp per score.
+    float psum = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[t][r] * c2;
-          if (need_mask) {
-            const int key = kb + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= N || (CAUSAL && key > qrow)) x = -INFINITY;
-          }
-          s[t][r] = x;
-          mloc = fmaxf(mloc, x);
-        }
-      mloc = pair_max(mloc);
-      const float m_new = fmaxf(m_run, mloc);
-      const float mb = (m_new == -INFINITY) ? 0.f : m_new;  // never form -inf - -inf
-      const float alpha = fast_exp2(m_run - mb);
-      float psum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(s[t][r] - mb);
-          s[t][r] = p;
-          psum += p;
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      // Rescale O~ only when some row's max moved (alpha == 1 otherwise).
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[t][r], c2, -mb));
+        s[t][r] = p;
+        psum += p;
       }
-      // P as B operand: 16-key chunk cc of subtile t = registers 8cc..8cc+7,
-      // i.e. keys 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3); the A operand
-      // V^T takes the same keys for column 32dt + l%32 with two transposing
-      // reads.
-      u32x4 pp[2][2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int h = 0; h < 4; ++h)
-            pp[t][cc][h] = pack2<T>(s[t][8 * cc + 2 * h], s[t][8 * cc + 2 * h + 1]);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // Rescale O~ only when some row's max moved (alpha == 1 otherwise).
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            const uint16_t *src = Vs + tr_off + (32 * t + 16 * cc) * C::VS + 32 * dt;
-            const u32x4 a = cat(ld_tr16(src), ld_tr16(src + 8 * C::VS));
-            o[dt] = mfma32<T>(a, pp[t][cc], o[dt]);
-          }
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
-    if (kt + 1 < ntiles) swrite(buf ^ 1);
+    // P as B operand: 16-key chunk cc of subtile t = registers 8cc..8cc+7,
+    // i.e. keys 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3); the A operand
+    // V^T takes the same keys for column 32dt + l%32 with two transposing
+    // reads.
+    u32x4 pp[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          pp[t][cc][h] = pack2<T>(s[t][8 * cc + 2 * h], s[t][8 * cc + 2 * h + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const uint16_t *src = Vs + voff[dt] + (32 * t + 16 * cc) * D;
+          o[dt] = mfma32<T>(cat(ld_tr16(src), ld_tr16(src + 8 * D)), pp[t][cc], o[dt]);
+        }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto tile_step = [&](const uint16_t *Ks, const uint16_t *Vs, int kt) __attribute__((always_inline)) {
+    const int kb = kt * C::BC;
+    // Under the causal mask a wave whose rows all precede the tile skips it.
+    if (CAUSAL && kb > wq0 + 31) return;
+    if ((kb + C::BC > N) || (CAUSAL && kb + C::BC - 1 > wq0))
+      step(Ks, Vs, kb, std::true_type{});
+    else
+      step(Ks, Vs, kb, std::false_type{});
+  };
+
+  // Double-buffered sweep, unrolled by two so each half names its buffers:
+  // wait for this wave's loads of the tile, barrier (every wave's loads have
+  // landed and every wave is done with the other buffer), issue the next
+  // tile's loads into the other buffer, compute.
+  issue(K0, V0, 0);
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    wait_vmem_all();
+    __syncthreads();
+    if (kt + 1 < ntiles) issue(K1, V1, kt + 1);
+    tile_step(K0, V0, kt);
+    if (kt + 1 >= ntiles) break;
+    wait_vmem_all();
+    __syncthreads();
+    if (kt + 2 < ntiles) issue(K0, V0, kt + 2);
+    tile_step(K1, V1, kt + 1);
   }
 
   // Epilogue: O = O~ / l, LSE = (m + log2 l) * ln 2.
