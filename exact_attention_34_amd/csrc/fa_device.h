@@ -55,6 +55,21 @@ __device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + lo(x) + hi(x) for a dword of two 16-bit values (v_dot2c_f32_{bf16,f16}
+// against (1, 1)): sums the rounded values in fp32.
+template <typename T>
+__device__ __forceinline__ float add_pair(uint32_t x, float acc);
+template <>
+__device__ __forceinline__ float add_pair<BF16>(uint32_t x, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
+}
+template <>
+__device__ __forceinline__ float add_pair<F16>(uint32_t x, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), one, acc, false);
+}
+
 // 16-bit -> fp32.
 template <typename T>
 __device__ __forceinline__ float to_f32(uint16_t h);

@@ -35,6 +35,9 @@
 
 namespace fa {
 
+// Slack of the running reference max (base-2 units): P <= 2^kMaxSlack.
+constexpr float kMaxSlack = 8.f;
+
 template <int D>
 struct FwdCfg {
   static constexpr int kThreads = 256;       // 4 waves
@@ -199,50 +202,48 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
         mloc = fmaxf(mloc, s[t][r]);
       }
     mloc = pair_max(mloc);
-    const float m_new = fmaxf(m_run, mloc * c2);
-    const float mb = (m_new == -INFINITY) ? 0.f : m_new;  // never form -inf - -inf
-    const float alpha = fast_exp2(m_run - mb);
-    // P = 2^(s*c2 - m); one FMA and one exp per score.
-    float psum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(s[t][r], c2, -mb));
-        s[t][r] = p;
-        psum += p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // Rescale O~ only when some row's max moved (alpha == 1 otherwise).
+    // Reference max: moved only when the row max exceeds it by more than
+    // kMaxSlack (base 2). Any reference gives the same O~ / l; keeping it
+    // bounds P = 2^(s*c2 - m) by 2^kMaxSlack and makes the O~ rescale rare.
+    const float m_cand = fmaxf(m_run, mloc * c2);
+    float alpha = 1.f;
+    if (m_cand > m_run + kMaxSlack) {
+      alpha = fast_exp2(m_run - m_cand);
+      m_run = m_cand;
+    }
+    const float mb = (m_run == -INFINITY) ? 0.f : m_run;  // never form -inf - -inf
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
-    // P as B operand: 16-key chunk cc of subtile t = registers 8cc..8cc+7,
-    // i.e. keys 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3); the A operand
-    // V^T takes the same keys for column 32dt + l%32 with two transposing
-    // reads.
-    u32x4 pp[2][2];
+    // P = 2^(s*c2 - m), one FMA and one exp per score, rounded to T in pairs:
+    // 16-key chunk cc of subtile t = registers 8cc..8cc+7, i.e. keys
+    // 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3) -- the B operand of
+    // O~^T += V^T P^T. The A operand V^T takes the same keys for column
+    // 32dt + l%32 with two transposing reads. The row sum adds the fp32
+    // values (the normaliser and LSE keep fp32 accuracy).
+    float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
+      for (int cc = 0; cc < 2; ++cc) {
+        u32x4 pp;
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-          pp[t][cc][h] = pack2<T>(s[t][8 * cc + 2 * h], s[t][8 * cc + 2 * h + 1]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const uint16_t *src = Vs + voff[dt] + (32 * t + 16 * cc) * D;
-          o[dt] = mfma32<T>(cat(ld_tr16(src), ld_tr16(src + 8 * D)), pp[t][cc], o[dt]);
+        for (int h = 0; h < 4; ++h) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[t][8 * cc + 2 * h], c2, -mb));
+          const float p1 = fast_exp2(__builtin_fmaf(s[t][8 * cc + 2 * h + 1], c2, -mb));
+          pp[h] = pack2<T>(p0, p1);
+          psum += p0 + p1;
         }
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) {
+          const uint16_t *src = Vs + voff[dt] + (32 * t + 16 * cc) * D;
+          o[dt] = mfma32<T>(cat(ld_tr16(src), ld_tr16(src + 8 * D)), pp, o[dt]);
+        }
+      }
+    l_run = l_run * alpha + psum;
     __builtin_amdgcn_sched_barrier(0);
   };
   auto tile_step = [&](const uint16_t *Ks, const uint16_t *Vs, int kt) __attribute__((always_inline)) {
