@@ -17,6 +17,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Zero accumulator: starting an MFMA chain from it lets the compiler use the
+// instruction's inline-zero accumulator operand.
+constexpr f32x16 kZero16 = {};
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -180,6 +184,13 @@ __device__ __forceinline__ void buffer_load_lds16(const i32x4 &rsrc, int voffset
                                                   void *lds_base) {
   raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_base, 16, voffset,
                       soffset, 0, 0);
+}
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations, then s_barrier. Unlike __syncthreads() it does not wait for
+// outstanding vector-memory operations (direct-to-LDS loads of another
+// buffer, atomics), which may keep flying across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 // Wait until every vector-memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
