@@ -1,20 +1,24 @@
 """Throughput benchmark: exact attention forward + backward on one MI355X.
 
 One step is one pass of the whole path over one batch: fa_fwd (O, LSE), then
-fa_bwd's three stages (D = rowsum(dO o O), the blocked backward, the dQ
-conversion). The workload is the Llama-2-7B-shaped causal attention layer
+fa_bwd's three stages (D = rowsum(dO o O), the dK/dV sweep over key blocks,
+the dQ sweep over query blocks). The workload is the Llama-2-7B-shaped causal attention layer
 (batch 16, 32 heads, N = 2048, d = 128, bf16; rotary Q/K, dO ~ N(0, 0.01)),
 with inputs resident in device memory before the timed region.
 
 FLOPs follow the pages' accounting: forward 4*B*H*N^2*d, backward
 10*B*H*N^2*d (the recompute of S included), halved under the causal mask.
+The dQ sweep recomputes S and dP a second time; those products are not
+counted (of the backward's 10, the dK/dV sweep is credited with 8 -- S, dP,
+dV, dK -- and the dQ sweep with 2 -- the dS K product).
 
 Prints ONE JSON line. Besides the required keys it carries:
-  roofline      the dominant kernel (backward main) against the bf16 dense MFMA
-                peak, its duration measured with HIP events on the launch
-                stream inside the timed region; HBM traffic from the committed
-                rocprofv3 counter summary when it was taken on the current
-                kernel source, else null;
+  roofline      the dominant kernel (the backward sweep with the longer
+                duration) against the bf16 dense MFMA peak, its duration
+                measured with HIP events on the launch stream inside the
+                timed region; HBM traffic from the committed rocprofv3 counter
+                summary when it was taken on the current kernel source, else
+                null;
   cpu_baseline  the fp64 oracle timed on host cores on a sample of the same
                 workload (also used as a parity spot-check of the timed run);
   sweep         forward and forward+backward TFLOPS for bf16 d = 128 at
@@ -33,7 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOPS (fwd; fwd+bwd) bf16 d=128 N=2k–8k, % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_c5_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_c5_traffic.json")
 BWD_SRC = os.path.join(ROOT, "exact_attention_34_amd", "csrc", "fa_bwd.hip")
 
 
@@ -42,9 +46,9 @@ def _src_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic():
-    """Per-launch HBM bytes of the backward main kernel from the committed
-    counter summary, or None if absent or taken on other kernel source."""
+def _traffic(kernel):
+    """Per-launch HBM bytes of a backward kernel from the committed counter
+    summary, or None if absent or taken on other kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -52,7 +56,7 @@ def _traffic():
         return None
     if t.get("source_sha256_16") != _src_hash(BWD_SRC):
         return None
-    return t.get("bytes_per_launch")
+    return t.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
 
 def _inputs(w, torch, dev):
@@ -67,7 +71,6 @@ def _step_fns(fa, torch, w, d):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=d["q"].device)
     dq, dk, dv = (torch.empty_like(d["q"]) for _ in range(3))
     dvec = torch.empty((B, H, N), dtype=torch.float32, device=d["q"].device)
-    acc = torch.empty((B, H, N, D), dtype=torch.float32, device=d["q"].device)
     L = fa.lib()
     code = {torch.bfloat16: fa.BF16, torch.float16: fa.F16}[d["q"].dtype]
     P = lambda t: t.data_ptr()
@@ -83,16 +86,17 @@ def _step_fns(fa, torch, w, d):
                     P(lse), st))
 
     def pre():
-        ck(L.fa_bwd_preprocess(code, B, H, N, D, P(o), P(d["do"]), P(dvec), P(acc), st))
+        ck(L.fa_bwd_preprocess(code, B, H, N, D, P(o), P(d["do"]), P(dvec), st))
 
-    def main():
-        ck(L.fa_bwd_main(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(d["do"]),
-                         P(lse), P(dvec), w.scale, c, P(acc), P(dk), P(dv), st))
+    def dkdv():
+        ck(L.fa_bwd_dkdv(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(d["do"]),
+                         P(lse), P(dvec), w.scale, c, P(dk), P(dv), st))
 
-    def conv():
-        ck(L.fa_bwd_dq_convert(code, B, H, N, D, P(acc), w.scale, P(dq), st))
+    def dqs():
+        ck(L.fa_bwd_dq(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(d["do"]),
+                       P(lse), P(dvec), w.scale, c, P(dq), st))
 
-    return (fwd, pre, main, conv), {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    return (fwd, pre, dkdv, dqs), {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 
 def time_workload(fa, torch, w, steps, warmup, per_kernel=True):
@@ -103,7 +107,7 @@ def time_workload(fa, torch, w, steps, warmup, per_kernel=True):
         for f in fns:
             f()
     torch.cuda.synchronize()
-    names = ("fwd", "bwd_preprocess", "bwd_main", "bwd_dq_convert")
+    names = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
           for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
@@ -224,15 +228,18 @@ def main():
     value = flops_step / (ms_step * 1e-3) / 1e12
     fwd_tflops = w.fwd_flops() / (ms_fwd * 1e-3) / 1e12
 
-    main_ms = kern["bwd_main"]
-    main_flops = w.bwd_flops()
-    achieved = main_flops / (main_ms * 1e-3) / 1e12
-    traffic = _traffic()
-    roofline = {"kernel": "bwd_main_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+    # Algorithmic flops per launch of each backward sweep (see the header).
+    sweeps = {"bwd_dkdv": ("bwd_dkdv_kernel", 0.8 * w.bwd_flops()),
+              "bwd_dq": ("bwd_dq_kernel", 0.2 * w.bwd_flops())}
+    dom = max(sweeps, key=lambda k: kern[k])
+    kname, kflops = sweeps[dom]
+    achieved = kflops / (kern[dom] * 1e-3) / 1e12
+    roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "ms_per_launch": round(main_ms, 4),
-                "flops_per_launch": main_flops}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": _traffic(kname),
+                "ms_per_launch": round(kern[dom], 4),
+                "flops_per_launch": kflops}
+    bwd_ms = kern["bwd_preprocess"] + kern["bwd_dkdv"] + kern["bwd_dq"]
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -243,6 +250,7 @@ def main():
                       "d": w.d, "causal": w.causal, "global_batch": w.B, "seq_len": w.N,
                       "parallelism": "none (1 GPU)"},
            "fwd_tflops": round(fwd_tflops, 2),
+           "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 2),
            "fwd_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
            "fwdbwd_frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
            "kernel_ms": {k: round(v, 4) for k, v in kern.items()},

@@ -13,7 +13,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_main", "bwd_dq_convert",
+__all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq",
            "bwd_workspace_bytes", "FAError", "library_path", "lib",
            "F32", "F16", "BF16"]
 
@@ -55,12 +55,12 @@ def lib():
     L.fa_bwd_workspace_bytes.restype = z
     L.fa_bwd.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, p, p, z, p]
     L.fa_bwd.restype = i
-    L.fa_bwd_preprocess.argtypes = [i, i, i, i, i, p, p, p, p, p]
+    L.fa_bwd_preprocess.argtypes = [i, i, i, i, i, p, p, p, p]
     L.fa_bwd_preprocess.restype = i
-    L.fa_bwd_main.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, p, p]
-    L.fa_bwd_main.restype = i
-    L.fa_bwd_dq_convert.argtypes = [i, i, i, i, i, p, f, p, p]
-    L.fa_bwd_dq_convert.restype = i
+    L.fa_bwd_dkdv.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, p]
+    L.fa_bwd_dkdv.restype = i
+    L.fa_bwd_dq.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p]
+    L.fa_bwd_dq.restype = i
     _lib = L
     return L
 
@@ -128,23 +128,21 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None):
     return dq, dk, dv
 
 
-def bwd_preprocess(o, do, dvec, dq_acc):
-    """Stage 1 of bwd: dvec = rowsum(dO o O) (fp32 [B,H,N]), dq_acc = 0."""
+def bwd_preprocess(o, do, dvec):
+    """Stage 1 of bwd: dvec = rowsum(dO o O), fp32 [B, H, N]."""
     dt, B, H, N, d = _check_qkv(o, do)
-    _call("fa_bwd_preprocess", dt, B, H, N, d, _ptr(o), _ptr(do), _ptr(dvec),
-          _ptr(dq_acc), _stream(o))
+    _call("fa_bwd_preprocess", dt, B, H, N, d, _ptr(o), _ptr(do), _ptr(dvec), _stream(o))
 
 
-def bwd_main(q, k, v, do, lse, dvec, dq_acc, dk, dv, scale=None, causal=False):
-    """Stage 2 of bwd: dK, dV, and dq_acc += unscaled dS K."""
+def bwd_dkdv(q, k, v, do, lse, dvec, dk, dv, scale=None, causal=False):
+    """Stage 2 of bwd: dK and dV (key blocks outer)."""
     dt, B, H, N, d = _check_qkv(q, k, v, do, dk, dv)
-    _call("fa_bwd_main", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
-          _ptr(dvec), _scale(scale, d), int(bool(causal)), _ptr(dq_acc), _ptr(dk),
-          _ptr(dv), _stream(q))
+    _call("fa_bwd_dkdv", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+          _ptr(dvec), _scale(scale, d), int(bool(causal)), _ptr(dk), _ptr(dv), _stream(q))
 
 
-def bwd_dq_convert(dq_acc, dq, scale=None):
-    """Stage 3 of bwd: dq = dtype(scale * dq_acc)."""
-    dt, B, H, N, d = _check_qkv(dq)
-    _call("fa_bwd_dq_convert", dt, B, H, N, d, _ptr(dq_acc), _scale(scale, d), _ptr(dq),
-          _stream(dq))
+def bwd_dq(q, k, v, do, lse, dvec, dq, scale=None, causal=False):
+    """Stage 3 of bwd: dQ (query blocks outer)."""
+    dt, B, H, N, d = _check_qkv(q, k, v, do, dq)
+    _call("fa_bwd_dq", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+          _ptr(dvec), _scale(scale, d), int(bool(causal)), _ptr(dq), _stream(q))

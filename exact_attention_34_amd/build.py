@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-munsafe-fp-atomics", "-Wall"]
+                "-Wall"]
 
 
 def _compile(src, verbose):

@@ -71,40 +71,48 @@ int fa_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, 
 
 size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d) {
   if (check_shape(dtype, B, H, N, d, true) != FA_OK) return 0;
-  return d_bytes(B, H, N) + (size_t)B * H * N * d * sizeof(float);
+  return d_bytes(B, H, N);
 }
 
 int fa_bwd_preprocess(int dtype, int B, int H, int N, int d, const void *O, const void *dO,
-                      float *Dvec, float *dQacc, void *stream) {
+                      float *Dvec, void *stream) {
   const int rc = check_shape(dtype, B, H, N, d, true);
   if (rc != FA_OK) return rc;
-  if (!tensor_ok(O) || !tensor_ok(dO) || !vec_ok(Dvec) || !tensor_ok(dQacc))
-    return FA_ERR_INVALID_ARG;
-  return status(fa::launch_bwd_preprocess(dtype, B, H, N, d, O, dO, Dvec, dQacc,
-                                          (hipStream_t)stream));
+  if (!tensor_ok(O) || !tensor_ok(dO) || !vec_ok(Dvec)) return FA_ERR_INVALID_ARG;
+  return status(fa::launch_bwd_preprocess(dtype, B, H, N, d, O, dO, Dvec, (hipStream_t)stream));
 }
 
-int fa_bwd_main(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
-                const void *V, const void *dO, const float *LSE, const float *Dvec,
-                float scale, int causal, float *dQacc, void *dK, void *dV, void *stream) {
+// Checks shared by the two gradient sweeps (everything but the outputs).
+static int check_sweep(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                       const void *V, const void *dO, const float *LSE, const float *Dvec,
+                       float scale, int causal) {
   int rc = check_shape(dtype, B, H, N, d, true);
   if (rc != FA_OK) return rc;
   if ((rc = check_scale_causal(scale, causal)) != FA_OK) return rc;
   if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(dO) || !vec_ok(LSE) ||
-      !vec_ok(Dvec) || !tensor_ok(dQacc) || !tensor_ok(dK) || !tensor_ok(dV))
+      !vec_ok(Dvec))
     return FA_ERR_INVALID_ARG;
-  return status(fa::launch_bwd_main(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
-                                    dQacc, dK, dV, (hipStream_t)stream));
+  return FA_OK;
 }
 
-int fa_bwd_dq_convert(int dtype, int B, int H, int N, int d, const float *dQacc, float scale,
-                      void *dQ, void *stream) {
-  const int rc = check_shape(dtype, B, H, N, d, true);
+int fa_bwd_dkdv(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                const void *V, const void *dO, const float *LSE, const float *Dvec, float scale,
+                int causal, void *dK, void *dV, void *stream) {
+  const int rc = check_sweep(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal);
   if (rc != FA_OK) return rc;
-  if (!(isfinite(scale) && scale > 0.f)) return FA_ERR_INVALID_ARG;
-  if (!tensor_ok(dQacc) || !tensor_ok(dQ)) return FA_ERR_INVALID_ARG;
-  return status(fa::launch_bwd_dq_convert(dtype, B, H, N, d, dQacc, scale, dQ,
-                                          (hipStream_t)stream));
+  if (!tensor_ok(dK) || !tensor_ok(dV)) return FA_ERR_INVALID_ARG;
+  return status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
+                                    dK, dV, (hipStream_t)stream));
+}
+
+int fa_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
+              const void *dO, const float *LSE, const float *Dvec, float scale, int causal,
+              void *dQ, void *stream) {
+  const int rc = check_sweep(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal);
+  if (rc != FA_OK) return rc;
+  if (!tensor_ok(dQ)) return FA_ERR_INVALID_ARG;
+  return status(fa::launch_bwd_dq(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal, dQ,
+                                  (hipStream_t)stream));
 }
 
 int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
@@ -119,15 +127,14 @@ int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, 
     return FA_ERR_INVALID_ARG;
   if (workspace_bytes < fa_bwd_workspace_bytes(dtype, B, H, N, d)) return FA_ERR_WORKSPACE;
   float *Dvec = (float *)workspace;
-  float *dQacc = (float *)((char *)workspace + d_bytes(B, H, N));
   hipStream_t st = (hipStream_t)stream;
-  if ((rc = status(fa::launch_bwd_preprocess(dtype, B, H, N, d, O, dO, Dvec, dQacc, st))) !=
-      FA_OK)
+  if ((rc = status(fa::launch_bwd_preprocess(dtype, B, H, N, d, O, dO, Dvec, st))) != FA_OK)
     return rc;
-  if ((rc = status(fa::launch_bwd_main(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
-                                       dQacc, dK, dV, st))) != FA_OK)
+  if ((rc = status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
+                                       dK, dV, st))) != FA_OK)
     return rc;
-  return status(fa::launch_bwd_dq_convert(dtype, B, H, N, d, dQacc, scale, dQ, st));
+  return status(
+      fa::launch_bwd_dq(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal, dQ, st));
 }
 
 }  // extern "C"

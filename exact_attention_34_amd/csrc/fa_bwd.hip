@@ -1,29 +1,27 @@
 // fa_bwd.hip -- backward pass of exact attention on gfx950.
 //
 // Follows the blocked backward of the "Flash Attention" notes (section 3,
-// part 4.2, and the backward-derivation page, part 6), with the two loops
-// swapped: each workgroup owns a block of KB keys, keeps dK and dV for them in
-// registers, and walks the query tiles. For each tile it recomputes
+// part 4.2, and the backward-derivation page, part 6). Per pair of tiles it
+// recomputes
 //   S = Q K^T,  P = exp(scale*S - LSE)            (section 3, part 4.1)
-// and accumulates
+// and forms
 //   dV += P^T dO,  dP = dO V^T,  dS = P o (dP - D),
 //   dK += dS^T Q,  dQ += dS K                      (derivation, parts 3-4)
 // with D = rowsum(dO o O) precomputed by a separate pass (derivation, part 5).
-// dQ rows receive contributions from every key block, so they are summed with
-// fp32 atomics into a workspace and converted (times scale) at the end; the
-// scale of dK is applied in the epilogue (the Ascend recompute article writes
-// 1/sqrt(d_k) into both dQ and dK).
+// The scale enters dQ and dK once, at the end (the Ascend recompute article
+// writes 1/sqrt(d_k) into both).
 //
-// Per wave (32 keys): K and V stay in VGPRs as the B operands of S = Q K^T and
-// dP = dO V^T. S/P and dP/dS come out of the MFMA with one key per lane
-// (column l % 32) and 16 query rows per lane, which is exactly the B-operand
-// layout of dV^T = dO^T P and dK^T = Q^T dS, so P and dS never leave
-// registers for those two products; the dO^T and Q^T operands are read from
-// the row-major tiles with transposing LDS reads (ds_read_b64_tr_b16). dS is
-// also written to LDS, where each wave reads a 32x32 (query, column) tile of
-// dQ = dS K over all KB keys and adds it into the fp32 workspace. Query tiles
-// (Q, dO, LSE, D) are double-buffered in LDS and filled by direct buffer ->
-// LDS loads issued one tile ahead.
+// The pages' loop nest (keys outer, queries inner, dQ read-modified-written
+// per pair of tiles) makes every key block add into every dQ row. Here the
+// work is split into two sweeps that each own their outputs, so no partial
+// sum leaves a workgroup and no atomics are needed:
+//   * bwd_dkdv_kernel: a workgroup owns a block of KB keys and walks the
+//     query tiles, keeping dK and dV in registers (the pages' outer loop);
+//   * bwd_dq_kernel: a workgroup owns a block of query rows and walks the
+//     key tiles, keeping dQ in registers (recomputing S, P, dP, dS).
+// The second sweep repeats the S and dP products (7 instead of 5 matrix
+// products per tile pair); on this chip that is cheaper than summing dQ
+// through fp32 atomics in L2, and every gradient is deterministic.
 
 #include <type_traits>
 
@@ -33,13 +31,12 @@
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// D_i = sum_k dO_ik O_ik (fp32), and dQacc = 0.
+// D_i = sum_k dO_ik O_ik (fp32).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict__ O,
                                                       const uint16_t *__restrict__ dO,
-                                                      float *__restrict__ Dvec,
-                                                      float *__restrict__ dQacc, long rows) {
+                                                      float *__restrict__ Dvec, long rows) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;
   const int tid = threadIdx.x;
@@ -54,9 +51,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
       acc += to_f32<T>((uint16_t)(a[h] & 0xffffu)) * to_f32<T>((uint16_t)(b[h] & 0xffffu));
       acc += to_f32<T>((uint16_t)(a[h] >> 16)) * to_f32<T>((uint16_t)(b[h] >> 16));
     }
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4 *)(dQacc + row * D + 8 * sub) = z;
-    *(f32x4 *)(dQacc + row * D + 8 * sub + 4) = z;
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
@@ -64,29 +58,64 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// dQ = dtype(scale * dQacc)
+// Shared tile layout.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float *__restrict__ acc,
-                                                         uint16_t *__restrict__ dQ, long n8,
-                                                         float scale) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *(const f32x4 *)(acc + 8 * i);
-  const f32x4 b = *(const f32x4 *)(acc + 8 * i + 4);
-  u32x4 v;
-  v[0] = pack2<T>(a[0] * scale, a[1] * scale);
-  v[1] = pack2<T>(a[2] * scale, a[3] * scale);
-  v[2] = pack2<T>(b[0] * scale, b[1] * scale);
-  v[3] = pack2<T>(b[2] * scale, b[3] * scale);
-  st128(dQ + 8 * i, v);
+// Q, dO, K and V tiles in LDS are unpadded, row-major at 16-byte-chunk
+// granularity, with the chunk index XOR-ed by swz(row). They are read two
+// ways: row-wise (16 consecutive rows, one chunk each, per quarter-wave) and
+// with transposing loads (4 consecutive rows x 4 chunks per half-wave). swz
+// maps both access groups onto 16 distinct four-bank groups of the 64-bank
+// LDS. It depends on row % 16 only.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Per-lane LDS byte offsets into such a tile. The swizzle only touches
+// address bits that the row and column terms of one access leave zero, so
+// every access is a per-lane base XOR-ed with a compile-time constant:
+//  * row-wise read of row 32a + l%32, 16-byte chunk 2c + l/32:
+//      (row_base() ^ 32 c) + 64 D a;
+//  * transposing read (ds_read_b64_tr_b16) of rows rb + (l%16)/4, columns
+//    32 dt + 16 ((l/16)%2) + 4 (l%4) .. +3, for rb = 16 b + r0 with
+//    r0 < 16:  (tr_base(r0) ^ 64 dt) + 32 D b.
+// The XOR terms stay below the row terms, so the row terms add: they go into
+// the tile pointer and from there into the instructions' immediate offsets,
+// and only one register per XOR constant is needed.
+template <int D>
+__device__ __forceinline__ int row_base(int lane) {
+  const int l32 = lane & 31, g = lane >> 5;
+  const int f = swz<D>(l32);
+  return l32 * 2 * D + 16 * (g ^ (f & 1)) + 32 * (f >> 1);
+}
+template <int D>
+__device__ __forceinline__ int tr_base(int r0, int lane) {
+  const int row = r0 + (lane & 15) / 4;
+  const int cq = 2 * ((lane >> 4) & 1) + (lane & 3) / 2;  // chunk within a 64-byte column group
+  const int f = swz<D>(row);
+  return row * 2 * D + 16 * (cq ^ (f & 3)) + 8 * (lane & 1) + 64 * (f >> 2);
+}
+
+__device__ __forceinline__ const uint16_t *at(const uint16_t *tile, int byte_off) {
+  return (const uint16_t *)((const char *)tile + byte_off);
+}
+
+// LDS chunk p (0 .. rows * CPR - 1) of a swizzled tile holds global chunk
+// (p % CPR) ^ swz(row) of row p / CPR: byte offset of that chunk in a dense
+// row-major source with D elements per row.
+template <int D>
+__device__ __forceinline__ int src_of_chunk(int p) {
+  constexpr int CPR = D / 8;
+  const int r = p / CPR, sw = p % CPR;
+  return 2 * (r * D + 8 * (sw ^ swz<D>(r)));
 }
 
 // ---------------------------------------------------------------------------
-// Main backward kernel.
+// dK, dV: key blocks outer, query tiles inner.
 // ---------------------------------------------------------------------------
 template <int D>
-struct BwdCfg {
+struct DkdvCfg {
   static constexpr int kThreads = 512;               // 8 waves, two per SIMD
   static constexpr int KB = 128;                     // keys per workgroup, 32 per wave pair
   static constexpr int BR = (D == 128) ? 64 : 128;   // query rows per step
@@ -96,37 +125,29 @@ struct BwdCfg {
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int QTILE = BR * D;               // 16-bit elements per Q or dO tile
   static constexpr int LPW = BR * CPR / kThreads;    // direct loads per wave per tile and tensor
-  static constexpr int SS = KB + 8;                  // dS row stride
   static_assert(LPW == 2, "two direct loads per wave per tile");
-  static_assert((BR / 32) * NDT == 8, "one 32x32 dQ tile per wave");
 };
 
-// Q, dO, K and V tiles are unpadded, row-major at 16-byte-chunk granularity,
-// with the chunk index XOR-ed by swz_q(row). They are read two ways: row-wise
-// (16 consecutive rows, one chunk each, per quarter-wave) and with
-// transposing loads (4 consecutive rows x 4 chunks per half-wave). swz_q maps
-// both access groups onto 16 distinct four-bank groups of the 64-bank LDS.
-template <int D>
-__device__ __forceinline__ int swz_q(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
+// Per wave: a slice of 32 keys (column l % 32 of every S/P/dP/dS product)
+// and one half of each query tile. S and dP come out of the MFMA with one key
+// per lane and 16 query rows per lane, which is exactly the B-operand layout
+// of dV^T = dO^T P and dK^T = Q^T dS, so P and dS never leave registers; the
+// dO^T and Q^T operands are read from the row-major tiles with transposing
+// LDS reads. The two waves of a key slice sum their dK, dV partials through
+// LDS at the end. Query tiles (Q, dO, LSE, D) are double-buffered and filled
+// by direct buffer -> LDS loads issued one tile ahead.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void bwd_main_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Dvec, float *__restrict__ dQacc,
-    uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int N, int nkb, int total, float c2,
-    float scale) {
-  using C = BwdCfg<D>;
-  // Double buffers for the query tiles (named separately so the compiler can
-  // tell the direct loads into one from the reads of the other), their fp32
-  // LSE and D rows, dS, and the key block's K and V.
-  __shared__ __attribute__((aligned(1024))) uint16_t Q0[C::QTILE], O0[C::QTILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t Q1[C::QTILE], O1[C::QTILE];
-  __shared__ __attribute__((aligned(256))) float L0[2 * C::BR], L1[2 * C::BR];
-  __shared__ __attribute__((aligned(16))) uint16_t dSs[C::BR * C::SS];
+    const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dK,
+    uint16_t *__restrict__ dV, int N, int nkb, int total, float c2, float scale) {
+  using C = DkdvCfg<D>;
+  // Double buffers for the query tiles: buffer b holds Q at
+  // qo + 2*b*QTILE, dO right after it, and LSE, D rows at lv + 2*b*BR. Then
+  // the key block's K and V.
+  __shared__ __attribute__((aligned(1024))) uint16_t qo[4 * C::QTILE];
+  __shared__ __attribute__((aligned(256))) float lv[4 * C::BR];
   __shared__ __attribute__((aligned(1024))) uint16_t Kst[C::KB * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vst[C::KB * D];
 
@@ -143,13 +164,12 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(
   const int mykey = wk0 + l32;   // key of this lane's S/P column
   const size_t base = (size_t)bh * N * D;
   const uint16_t *Qh = Q + base, *Kh = K + base, *Vh = V + base, *dOh = dO + base;
-  float *dQh = dQacc + base;
 
   // K and V of the key block into LDS; keys past N read row N - 1 (masked).
   for (int c = tid; c < C::KB * C::CPR; c += C::kThreads) {
     const int row = c / C::CPR, ch = c % C::CPR;
     const int key = min(k0 + row, N - 1);
-    const int pos = row * D + 8 * (ch ^ swz_q<D>(row));
+    const int pos = row * D + 8 * (ch ^ swz<D>(row));
     st128(Kst + pos, ld128(Kh + (size_t)key * D + 8 * ch));
     st128(Vst + pos, ld128(Vh + (size_t)key * D + 8 * ch));
   }
@@ -170,69 +190,43 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(
 #pragma unroll
   for (int i = 0; i < C::LPW; ++i) {
     const int p = (w * C::LPW + i) * 64 + lane;
-    const int r = p / C::CPR, sw = p % C::CPR;
-    grow[i] = r;
-    gq[i] = 2 * (r * D + 8 * (sw ^ swz_q<D>(r)));
+    grow[i] = p / C::CPR;
+    gq[i] = src_of_chunk<D>(p);
   }
-  auto issue = [&](uint16_t *Qb, uint16_t *Ob, float *Lb, int it) __attribute__((always_inline)) {
+  auto issue = [&](int b, int it) __attribute__((always_inline)) {
+    uint16_t *Qb = qo + 2 * b * C::QTILE, *Ob = Qb + C::QTILE;
     const int q0 = it * C::BR;
     const int soff = q0 * D * 2;
     if (q0 + C::BR <= N) {
 #pragma unroll
       for (int i = 0; i < C::LPW; ++i) {
-        buffer_load_lds16(qrs, gq[i], soff, Qb + (w * C::LPW + i) * 512);
-        buffer_load_lds16(ors, gq[i], soff, Ob + (w * C::LPW + i) * 512);
+        dma_lds16(qrs, gq[i], soff, Qb + (w * C::LPW + i) * 512);
+        dma_lds16(ors, gq[i], soff, Ob + (w * C::LPW + i) * 512);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::LPW; ++i) {
         const int shift = 2 * D * (min(q0 + grow[i], N - 1) - q0 - grow[i]);  // <= 0
-        buffer_load_lds16(qrs, gq[i] + shift, soff, Qb + (w * C::LPW + i) * 512);
-        buffer_load_lds16(ors, gq[i] + shift, soff, Ob + (w * C::LPW + i) * 512);
+        dma_lds16(qrs, gq[i] + shift, soff, Qb + (w * C::LPW + i) * 512);
+        dma_lds16(ors, gq[i] + shift, soff, Ob + (w * C::LPW + i) * 512);
       }
     }
     if (w < 2 * kVecParts) {
       const int vec = w / kVecParts, part = w % kVecParts;
       const int voff = 4 * (min(q0 + 64 * part + lane, N - 1) - q0);
-      raw_buffer_load_lds(vec == 0 ? lrs : drs,
-                          (__attribute__((address_space(3))) void *)(Lb + vec * C::BR + 64 * part),
-                          4, voff, 4 * q0, 0, 0);
+      dma_lds4(vec == 0 ? lrs : drs, voff, 4 * q0, lv + 2 * b * C::BR + vec * C::BR + 64 * part);
     }
   };
 
-  // Per-lane LDS byte offsets. The swizzle only touches address bits that
-  // the row and column terms of one access leave zero, so every access is a
-  // per-lane base XOR-ed with a compile-time constant (one v_xor per read):
-  //  * row-wise reads (row 32qt + l%32, 16-byte chunk 2c + g):
-  //      rb ^ (32 c + 64 D qt);
-  //  * transposing reads (rows rowbase + (l%16)/4 of a 16-row block, columns
-  //    32dt + 16((l/16)%2) + 4(l%4)): base(rowbase) ^ (64 dt + 2 D * block row),
-  //    with one base per half of an operand (the swizzle depends on the row).
-  const int jr = (lane & 15) / 4;
-  const int cq = 2 * ((lane >> 4) & 1) + (lane & 3) / 2;  // chunk within a 64-byte column group
-  auto tr_base = [&](int row) {
-    const int f = swz_q<D>(row);
-    return row * 2 * D + 16 * (cq ^ (f & 3)) + 8 * (lane & 1) + 64 * (f >> 2);
-  };
-  int rb;
-  {
-    const int f = swz_q<D>(l32);
-    rb = l32 * 2 * D + 16 * (g ^ (f & 1)) + 32 * (f >> 1);
-  }
-  // Row-wise reads of this wave's keys 32 ks + l%32 in the K and V tiles.
-  const int kb_off = rb ^ (64 * D * ks);
+  // Row-wise reads: this wave's keys 32 ks + l%32 of the K and V tiles, and
+  // its query rows (subtiles qh*NQW ..) of the Q and dO tiles.
+  const int rb = row_base<D>(lane);
+  const int kb_off = rb | (64 * D * ks);
+  const int qb_off = rb | (64 * D * C::NQW * qh);
   // Q^T / dO^T operands: rows 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3)
-  // of a 32-row subtile (the P / dS register layout).
-  const int tb1 = tr_base(4 * g + jr), tb2 = tr_base(8 + 4 * g + jr);
-  // This wave's dQ tile: query subtile dq_qt, columns 32 dq_dt .. +31. Its K
-  // operand: keys 16c + 8g + (0..3) and 16c + 8g + 4 + (0..3).
-  const int dq_qt = w / C::NDT, dq_dt = w % C::NDT;
-  const int tk1 = tr_base(8 * g + jr) ^ (64 * dq_dt), tk2 = tr_base(8 * g + 4 + jr) ^ (64 * dq_dt);
-  // dQ atomics: this lane's element of row 8(r/4) + 4g + r%4 of its tile.
-  const int dq_lane = (32 * dq_qt + 4 * g) * D + 32 * dq_dt + l32;
-  auto at = [](const uint16_t *tile, int byte_off) {
-    return (const uint16_t *)((const char *)tile + byte_off);
-  };
+  // of a 32-row subtile (the P / dS register layout), in this wave's subtiles.
+  const int tb1 = tr_base<D>(4 * g, lane) | (64 * D * C::NQW * qh);
+  const int tb2 = tr_base<D>(8 + 4 * g, lane) | (64 * D * C::NQW * qh);
 
   // dK^T and dV^T partial sums (this wave's query half): column = key
   // (l % 32), rows = d.
@@ -260,26 +254,27 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(
   };
   using KM = std::integral_constant<int, 2 * C::NQW * C::NDT>;
 
-  // This wave's part of one query tile, up to dS in LDS. need_mask: the rows
-  // hold rows past N, keys past N, or (causal) keys after some row; masked
-  // scores become -inf, so P and dS are exactly 0 there. The mask is a
-  // VALU-only branch, so every MFMA accumulation runs on one code path.
-  auto part1 = [&](const uint16_t *Qs, const uint16_t *Os, const float *Lb, int q0,
-                   bool need_mask) __attribute__((always_inline)) {
+  // This wave's part of one query tile. need_mask: the rows hold rows past N,
+  // keys past N, or (causal) keys after some row; masked scores become -inf,
+  // so P and dS are exactly 0 there. The mask is a VALU-only branch, so every
+  // MFMA accumulation runs on one code path.
+  auto step = [&](const uint16_t *Qs, const uint16_t *Os, const float *Lb, int it)
+      __attribute__((always_inline)) {
+    const int q0 = it * C::BR;
+    const int q0w = q0 + 32 * C::NQW * qh;  // first query row of this wave
+    const bool need_mask =
+        (q0w + 32 * C::NQW > N) || (wk0 + 32 > N) || (CAUSAL && wk0 + 31 > q0w);
     __builtin_amdgcn_sched_barrier(0);
     // S = Q K^T and dP = dO V^T: column = key, rows 8(r/4) + 4g + r%4.
     f32x16 s[C::NQW], dp[C::NQW];
 #pragma unroll
     for (int t = 0; t < C::NQW; ++t) {
-      const int qt = qh * C::NQW + t;
-      s[t] = mfma32<T>(ld128(at(Qs, rb ^ (64 * D * qt))), ld128(at(Kst, kb_off)), kZero16);
-      dp[t] = mfma32<T>(ld128(at(Os, rb ^ (64 * D * qt))), ld128(at(Vst, kb_off)), kZero16);
 #pragma unroll
-      for (int c = 1; c < C::NCH; ++c) {
-        s[t] = mfma32<T>(ld128(at(Qs, rb ^ (32 * c + 64 * D * qt))),
-                         ld128(at(Kst, kb_off ^ (32 * c))), s[t]);
-        dp[t] = mfma32<T>(ld128(at(Os, rb ^ (32 * c + 64 * D * qt))),
-                          ld128(at(Vst, kb_off ^ (32 * c))), dp[t]);
+      for (int c = 0; c < C::NCH; ++c) {
+        s[t] = mfma32<T>(ld128(at(Qs + 32 * D * t, qb_off ^ (32 * c))),
+                         ld128(at(Kst, kb_off ^ (32 * c))), c == 0 ? kZero16 : s[t]);
+        dp[t] = mfma32<T>(ld128(at(Os + 32 * D * t, qb_off ^ (32 * c))),
+                          ld128(at(Vst, kb_off ^ (32 * c))), c == 0 ? kZero16 : dp[t]);
       }
     }
     // Operand reads two MFMAs ahead of their use (bounded register use).
@@ -329,9 +324,10 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
-          const int x = 64 * dt + 2 * D * (32 * (qh * C::NQW + t) + 16 * cc);
-          dv[dt] = mfma32<T>(cat(ld_tr16(at(Os, tb1 ^ x)), ld_tr16(at(Os, tb2 ^ x))),
-                             pk[t][cc], dv[dt]);
+          const uint16_t *src = Os + (32 * t + 16 * cc) * D;
+          dv[dt] = mfma32<T>(
+              cat(ld_tr16(at(src, tb1 ^ (64 * dt))), ld_tr16(at(src, tb2 ^ (64 * dt)))),
+              pk[t][cc], dv[dt]);
         }
     tr_pipeline(KM{});
     // dS = P o (dP - D)
@@ -357,92 +353,38 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
-          const int x = 64 * dt + 2 * D * (32 * (qh * C::NQW + t) + 16 * cc);
-          dk[dt] = mfma32<T>(cat(ld_tr16(at(Qs, tb1 ^ x)), ld_tr16(at(Qs, tb2 ^ x))),
-                             pk[t][cc], dk[dt]);
+          const uint16_t *src = Qs + (32 * t + 16 * cc) * D;
+          dk[dt] = mfma32<T>(
+              cat(ld_tr16(at(src, tb1 ^ (64 * dt))), ld_tr16(at(src, tb2 ^ (64 * dt)))),
+              pk[t][cc], dk[dt]);
         }
     tr_pipeline(KM{});
-    // dS (16-bit) to LDS, [query][key]
-#pragma unroll
-    for (int t = 0; t < C::NQW; ++t)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int r = 8 * cc + 2 * h;
-          const int ql = 32 * (qh * C::NQW + t) + 8 * (r >> 2) + 4 * g + (r & 3);
-          dSs[ql * C::SS + 32 * ks + l32] = (uint16_t)(pk[t][cc][h] & 0xffffu);
-          dSs[(ql + 1) * C::SS + 32 * ks + l32] = (uint16_t)(pk[t][cc][h] >> 16);
-        }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // This wave's dQ tile over the KB keys, added into the fp32 accumulator.
-  auto part2 = [&](int q0) __attribute__((always_inline)) {
-    f32x16 dq = kZero16;
-#pragma unroll
-    for (int c = 0; c < C::KB / 16; ++c) {
-      const int x = 2 * D * 16 * c;
-      dq = mfma32<T>(ld128(dSs + (32 * dq_qt + l32) * C::SS + 16 * c + 8 * g),
-                     cat(ld_tr16(at(Kst, tk1 ^ x)), ld_tr16(at(Kst, tk2 ^ x))),
-                     c == 0 ? kZero16 : dq);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int i = 0; i < C::KB / 16 - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    float *rowp = dQh + (size_t)q0 * D + dq_lane;
-    if (q0 + C::BR <= N) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) unsafeAtomicAdd(rowp + (8 * (r >> 2) + (r & 3)) * D, dq[r]);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 32 * dq_qt + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (q < N) unsafeAtomicAdd(rowp + (8 * (r >> 2) + (r & 3)) * D, dq[r]);
-      }
-    }
-  };
-  auto step = [&](const uint16_t *Qs, const uint16_t *Os, const float *Lb, int it, auto next)
-      __attribute__((always_inline)) {
-    const int q0 = it * C::BR;
-    const int q0w = q0 + 32 * C::NQW * qh;  // first query row of this wave
-    part1(Qs, Os, Lb, q0,
-          (q0w + 32 * C::NQW > N) || (wk0 + 32 > N) || (CAUSAL && wk0 + 31 > q0w));
-    // This wave has read the tile: load the next one into the other buffer
-    // (every wave finished reading that buffer before the previous dS
-    // barrier); the loads land during the dQ product and the atomics.
-    next();
-    barrier_lds();  // dS complete (the loads just issued keep flying)
-    part2(q0);
   };
 
   // Double-buffered sweep over the query tiles: wait for this wave's loads,
-  // barrier (every wave's loads landed; every wave done reading dS), compute
-  // (issuing the next tile's loads once the current tile has been read).
+  // barrier (every wave's loads landed; every wave is done with the other
+  // buffer), issue the next tile's loads into the other buffer, compute.
   __syncthreads();  // K and V staged
-  if (it0 < nq) issue(Q0, O0, L0, it0);
+  if (it0 < nq) issue(0, it0);
   for (int it = it0; it < nq; ++it) {
-    const bool odd = (it - it0) & 1;
+    const int b = (it - it0) & 1;
     wait_vmem_all();
     __syncthreads();
-    step(odd ? Q1 : Q0, odd ? O1 : O0, odd ? L1 : L0, it,
-         [&]() __attribute__((always_inline)) {
-           if (it + 1 < nq) {
-             if (odd) issue(Q0, O0, L0, it + 1);
-             else issue(Q1, O1, L1, it + 1);
-           }
-         });
+    if (it + 1 < nq) issue(b ^ 1, it + 1);
+    const uint16_t *Qs = qo + 2 * b * C::QTILE;
+    step(Qs, Qs + C::QTILE, lv + 2 * b * C::BR, it);
   }
 
   // Sum the two query halves' partial dK, dV (waves ks and ks + 4) through
-  // LDS: the second half writes its partials lane-major into free tiles.
+  // LDS: the second half writes its partials lane-major into free tiles
+  // (NDT * 16 * 64 floats each: a quarter of the query buffers, or half of K
+  // or V).
   __syncthreads();
-  float *xk = ks == 0 ? (float *)Q0 : ks == 1 ? (float *)Q1 : ks == 2 ? (float *)Kst : (float *)Vst;
-  float *xv = ks == 0 ? (float *)O0 : ks == 1 ? (float *)O1 : xk + C::NDT * 16 * 64;
+  constexpr int kPart = C::NDT * 16 * 64;
+  static_assert(4 * C::QTILE * 2 >= 4 * kPart * 4 && C::KB * D * 2 >= 2 * kPart * 4,
+                "partials fit in the freed tiles");
+  float *xk = ks < 2 ? (float *)qo + 2 * ks * kPart : ks == 2 ? (float *)Kst : (float *)Vst;
+  float *xv = xk + kPart;
   if (qh == 1) {
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
@@ -480,78 +422,295 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dQ: query blocks outer, key tiles inner.
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqCfg {
+  static constexpr int kThreads = 256;             // 4 waves
+  static constexpr int BR = 128;                   // query rows per workgroup, 32 per wave
+  static constexpr int BC = 64;                    // keys per tile, two 32-key halves
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = BC * D;              // 16-bit elements per K or V tile
+  static constexpr int NCH = D / 16;
+  static constexpr int NDT = D / 32;
+  static constexpr int LPW = BC * CPR / kThreads;  // direct loads per wave per tile and tensor
+};
+
+// Per wave: 32 query rows, whose Q and dO rows stay in VGPRs as the B
+// operands of S^T = K Q^T and dP^T = V dO^T; lane l owns query row l % 32, so
+// its LSE and D are two per-lane scalars. dS^T then has one query per lane
+// and 16 keys per lane in the B-operand layout of dQ^T += K^T dS^T, whose K^T
+// operand comes from the same K tile with transposing reads. K and V tiles
+// are double-buffered in LDS and filled by direct buffer -> LDS loads.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
+    const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dQ,
+    int N, int nqb, int total, float c2, float scale) {
+  using C = DqCfg<D>;
+  // Buffer b: K tile at kv + 2*b*TILE, V tile right after it.
+  __shared__ __attribute__((aligned(1024))) uint16_t kv[4 * C::TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int bh = tile / nqb;
+  int qb = tile - bh * nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
+  const int q0 = qb * C::BR;
+  const int wq0 = q0 + 32 * w;  // first query row of this wave
+  const int qrow = wq0 + l32;
+  const size_t base = (size_t)bh * N * D;
+  const uint16_t *Qh = Q + base, *Kh = K + base, *Vh = V + base, *dOh = dO + base;
+
+  // Rows past N are read from row N - 1 (always valid memory) and never
+  // stored.
+  const int qld = min(qrow, N - 1);
+  u32x4 qreg[C::NCH], oreg[C::NCH];
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    qreg[c] = ld128(Qh + (size_t)qld * D + 16 * c + 8 * g);
+    oreg[c] = ld128(dOh + (size_t)qld * D + 16 * c + 8 * g);
+  }
+  const float lse2 = LSE[(size_t)bh * N + qld] * kLog2e;
+  const float dd = Dvec[(size_t)bh * N + qld];
+
+  const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
+  const int ntiles = (kend + C::BC - 1) / C::BC;
+
+  const i32x4 krs = make_rsrc(Kh, (uint32_t)N * D * 2);
+  const i32x4 vrs = make_rsrc(Vh, (uint32_t)N * D * 2);
+  int gk[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) gk[i] = src_of_chunk<D>((w * C::LPW + i) * 64 + lane);
+  auto issue = [&](int b, int kt) __attribute__((always_inline)) {
+    uint16_t *Kb = kv + 2 * b * C::TILE, *Vb = Kb + C::TILE;
+    const int kb = kt * C::BC;
+    const int soff = kb * D * 2;
+    if (kb + C::BC <= N) {
+#pragma unroll
+      for (int i = 0; i < C::LPW; ++i) {
+        dma_lds16(krs, gk[i], soff, Kb + (w * C::LPW + i) * 512);
+        dma_lds16(vrs, gk[i], soff, Vb + (w * C::LPW + i) * 512);
+      }
+    } else {
+      // Tail tile: rows past N re-read row N - 1 (their keys are masked).
+#pragma unroll
+      for (int i = 0; i < C::LPW; ++i) {
+        const int r = ((w * C::LPW + i) * 64 + lane) / C::CPR;
+        const int shift = 2 * D * (min(kb + r, N - 1) - kb - r);  // <= 0
+        dma_lds16(krs, gk[i] + shift, soff, Kb + (w * C::LPW + i) * 512);
+        dma_lds16(vrs, gk[i] + shift, soff, Vb + (w * C::LPW + i) * 512);
+      }
+    }
+  };
+
+  const int rb = row_base<D>(lane);
+  // K^T operand of dQ^T: keys 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3)
+  // of a 32-key half (the dS^T register layout), column 32dt + l%32.
+  const int tb1 = tr_base<D>(4 * g, lane), tb2 = tr_base<D>(8 + 4 * g, lane);
+
+  f32x16 dq[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[dt][r] = 0.f;
+
+  // One 32-key half t of a tile. need_mask: the half holds keys past N or
+  // (causal) past this wave's first query row. The mask is a VALU-only
+  // branch, so every MFMA accumulation runs on one code path.
+  auto half = [&](const uint16_t *Ks, const uint16_t *Vs, int kb, int t, bool need_mask)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    // S^T = K Q^T and dP^T = V dO^T; lane: query qrow, keys 8(r/4)+4g+r%4.
+    f32x16 s = kZero16, dp = kZero16;
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) {
+      s = mfma32<T>(ld128(at(Ks + 32 * D * t, rb ^ (32 * c))), qreg[c], c == 0 ? kZero16 : s);
+      dp = mfma32<T>(ld128(at(Vs + 32 * D * t, rb ^ (32 * c))), oreg[c], c == 0 ? kZero16 : dp);
+    }
+    // One operand read per MFMA, issued four MFMAs ahead.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * C::NCH - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (key >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // P = 2^(S*scale*log2e - LSE*log2e), dS = P o (dP - D), rounded to T in
+    // pairs: 16-key chunk cc = registers 8cc .. 8cc+7.
+    u32x4 pk[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int r = 8 * cc + 2 * h;
+        const float p0 = fast_exp2(__builtin_fmaf(s[r], c2, -lse2));
+        const float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c2, -lse2));
+        pk[cc][h] = pack2<T>(p0 * (dp[r] - dd), p1 * (dp[r + 1] - dd));
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        const uint16_t *src = Ks + (32 * t + 16 * cc) * D;
+        dq[dt] = mfma32<T>(
+            cat(ld_tr16(at(src, tb1 ^ (64 * dt))), ld_tr16(at(src, tb2 ^ (64 * dt)))), pk[cc],
+            dq[dt]);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * C::NDT - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // One tile. DIAG: the tile may hold keys after some of this wave's rows
+  // (causal); a wave whose rows all precede a half skips it.
+  auto tile_step = [&](const uint16_t *Ks, const uint16_t *Vs, int kt, auto diag_tag)
+      __attribute__((always_inline)) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
+    const int kb = kt * C::BC;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int hb = kb + 32 * t;
+      if (DIAG && hb > wq0 + 31) continue;
+      half(Ks, Vs, kb, t, (hb + 32 > N) || (DIAG && hb + 31 > wq0));
+    }
+  };
+
+  // Double-buffered sweep over the key tiles: wait for this wave's loads,
+  // barrier (every wave's loads landed; every wave is done with the other
+  // buffer), issue the next tile's loads into the other buffer, compute.
+  // Under the causal mask the tiles from q0 on (the diagonal) run in a loop
+  // of their own, so that the skipping branches (whose joins would copy the
+  // dQ accumulators) stay out of the main loop.
+  const int nmain = CAUSAL ? min(ntiles, q0 / C::BC) : ntiles;
+  auto sweep_tile = [&](int kt, auto diag_tag) __attribute__((always_inline)) {
+    const int b = kt & 1;
+    wait_vmem_all();
+    __syncthreads();
+    if (kt + 1 < ntiles) issue(b ^ 1, kt + 1);
+    const uint16_t *Ks = kv + 2 * b * C::TILE;
+    tile_step(Ks, Ks + C::TILE, kt, diag_tag);
+  };
+  issue(0, 0);
+  for (int kt = 0; kt < nmain; ++kt) sweep_tile(kt, std::false_type{});
+  if constexpr (CAUSAL)
+    for (int kt = nmain; kt < ntiles; ++kt) sweep_tile(kt, std::true_type{});
+
+  // dQ = scale * dQ^T, transposed back: lane holds 4 consecutive columns of
+  // its row per register group.
+  if (qrow < N) {
+    uint16_t *dQrow = dQ + base + (size_t)qrow * D;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 v;
+        v[0] = pack2<T>(dq[dt][4 * i] * scale, dq[dt][4 * i + 1] * scale);
+        v[1] = pack2<T>(dq[dt][4 * i + 2] * scale, dq[dt][4 * i + 3] * scale);
+        *(u32x2 *)(dQrow + 32 * dt + 8 * i + 4 * g) = v;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-static hipError_t pre(long rows, const void *O, const void *dO, float *Dv, float *acc,
-                      hipStream_t st) {
+static hipError_t pre(long rows, const void *O, const void *dO, float *Dv, hipStream_t st) {
   constexpr int RPB = 256 / (D / 8);
   const long blocks = (rows + RPB - 1) / RPB;
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const uint16_t *)O, (const uint16_t *)dO, Dv, acc, rows);
+                     (const uint16_t *)O, (const uint16_t *)dO, Dv, rows);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_preprocess(int dtype, int B, int H, int N, int d, const void *O,
-                                 const void *dO, float *Dvec, float *dQacc, hipStream_t st) {
+                                 const void *dO, float *Dvec, hipStream_t st) {
   const long rows = (long)B * H * N;
   if (dtype == kBF16)
-    return d == 64 ? pre<BF16, 64>(rows, O, dO, Dvec, dQacc, st)
-                   : pre<BF16, 128>(rows, O, dO, Dvec, dQacc, st);
-  return d == 64 ? pre<F16, 64>(rows, O, dO, Dvec, dQacc, st)
-                 : pre<F16, 128>(rows, O, dO, Dvec, dQacc, st);
+    return d == 64 ? pre<BF16, 64>(rows, O, dO, Dvec, st) : pre<BF16, 128>(rows, O, dO, Dvec, st);
+  return d == 64 ? pre<F16, 64>(rows, O, dO, Dvec, st) : pre<F16, 128>(rows, O, dO, Dvec, st);
+}
+
+// Arguments shared by the two gradient sweeps.
+struct BwdArgs {
+  int BH, N;
+  const uint16_t *Q, *K, *V, *dO;
+  const float *LSE, *Dvec;
+  float c2, scale;
+};
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t dkdv(const BwdArgs &a, void *dK, void *dV, hipStream_t st) {
+  using C = DkdvCfg<D>;
+  const int nkb = (a.N + C::KB - 1) / C::KB;
+  const int total = nkb * a.BH;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
+                     a.Q, a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N, nkb,
+                     total, a.c2, a.scale);
+  return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL>
-static hipError_t bmain(int BH, int N, const void *Q, const void *K, const void *V,
-                        const void *dO, const float *LSE, const float *Dv, float c2, float scale,
-                        float *acc, void *dK, void *dV, hipStream_t st) {
-  using C = BwdCfg<D>;
-  const int nkb = (N + C::KB - 1) / C::KB;
-  const int total = nkb * BH;
-  hipLaunchKernelGGL((bwd_main_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
-                     (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                     (const uint16_t *)dO, LSE, Dv, acc, (uint16_t *)dK, (uint16_t *)dV, N, nkb,
-                     total, c2, scale);
+static hipError_t dq(const BwdArgs &a, void *dQ, hipStream_t st) {
+  using C = DqCfg<D>;
+  const int nqb = (a.N + C::BR - 1) / C::BR;
+  const int total = nqb * a.BH;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st, a.Q,
+                     a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dQ, a.N, nqb, total, a.c2,
+                     a.scale);
   return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t bmain_c(int causal, int BH, int N, const void *Q, const void *K, const void *V,
-                          const void *dO, const float *LSE, const float *Dv, float c2,
-                          float scale, float *acc, void *dK, void *dV, hipStream_t st) {
-  return causal ? bmain<T, D, true>(BH, N, Q, K, V, dO, LSE, Dv, c2, scale, acc, dK, dV, st)
-                : bmain<T, D, false>(BH, N, Q, K, V, dO, LSE, Dv, c2, scale, acc, dK, dV, st);
+static BwdArgs bwd_args(int B, int H, int N, const void *Q, const void *K, const void *V,
+                        const void *dO, const float *LSE, const float *Dvec, float scale) {
+  return BwdArgs{B * H, N, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                 (const uint16_t *)dO, LSE, Dvec, scale * kLog2e, scale};
 }
 
-hipError_t launch_bwd_main(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+// Instantiates F<T, D, CAUSAL>(args...) for the run-time dtype, d, causal.
+#define FA_DISPATCH(F, dtype, d, causal, ...)                                            \
+  ((dtype) == kBF16                                                                     \
+       ? ((d) == 64 ? ((causal) ? F<BF16, 64, true>(__VA_ARGS__)                        \
+                                : F<BF16, 64, false>(__VA_ARGS__))                      \
+                    : ((causal) ? F<BF16, 128, true>(__VA_ARGS__)                       \
+                                : F<BF16, 128, false>(__VA_ARGS__)))                    \
+       : ((d) == 64 ? ((causal) ? F<F16, 64, true>(__VA_ARGS__)                         \
+                                : F<F16, 64, false>(__VA_ARGS__))                       \
+                    : ((causal) ? F<F16, 128, true>(__VA_ARGS__)                        \
+                                : F<F16, 128, false>(__VA_ARGS__))))
+
+hipError_t launch_bwd_dkdv(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
                            const void *V, const void *dO, const float *LSE, const float *Dvec,
-                           float scale, int causal, float *dQacc, void *dK, void *dV,
-                           hipStream_t st) {
-  const int BH = B * H;
-  const float c2 = scale * kLog2e;
-  if (dtype == kBF16)
-    return d == 64 ? bmain_c<BF16, 64>(causal, BH, N, Q, K, V, dO, LSE, Dvec, c2, scale, dQacc,
-                                       dK, dV, st)
-                   : bmain_c<BF16, 128>(causal, BH, N, Q, K, V, dO, LSE, Dvec, c2, scale,
-                                        dQacc, dK, dV, st);
-  return d == 64 ? bmain_c<F16, 64>(causal, BH, N, Q, K, V, dO, LSE, Dvec, c2, scale, dQacc, dK,
-                                    dV, st)
-                 : bmain_c<F16, 128>(causal, BH, N, Q, K, V, dO, LSE, Dvec, c2, scale, dQacc,
-                                     dK, dV, st);
+                           float scale, int causal, void *dK, void *dV, hipStream_t st) {
+  const BwdArgs a = bwd_args(B, H, N, Q, K, V, dO, LSE, Dvec, scale);
+  return FA_DISPATCH(dkdv, dtype, d, causal, a, dK, dV, st);
 }
 
-hipError_t launch_bwd_dq_convert(int dtype, int B, int H, int N, int d, const float *dQacc,
-                                 float scale, void *dQ, hipStream_t st) {
-  const long n8 = (long)B * H * N * d / 8;
-  const long blocks = (n8 + 255) / 256;
-  if (dtype == kBF16)
-    hipLaunchKernelGGL((dq_convert_kernel<BF16>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       dQacc, (uint16_t *)dQ, n8, scale);
-  else
-    hipLaunchKernelGGL((dq_convert_kernel<F16>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       dQacc, (uint16_t *)dQ, n8, scale);
-  return hipGetLastError();
+hipError_t launch_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                         const void *V, const void *dO, const float *LSE, const float *Dvec,
+                         float scale, int causal, void *dQ, hipStream_t st) {
+  const BwdArgs a = bwd_args(B, H, N, Q, K, V, dO, LSE, Dvec, scale);
+  return FA_DISPATCH(dq, dtype, d, causal, a, dQ, st);
 }
+
+#undef FA_DISPATCH
 
 }  // namespace fa

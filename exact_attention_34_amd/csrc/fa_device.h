@@ -185,6 +185,44 @@ __device__ __forceinline__ void buffer_load_lds16(const i32x4 &rsrc, int voffset
   raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_base, 16, voffset,
                       soffset, 0, 0);
 }
+// The same direct loads (16 or 4 bytes per lane) written as inline assembly,
+// so the compiler does not track them: it would otherwise make every later
+// LDS read that it cannot prove disjoint from the destination (e.g. a buffer
+// chosen at run time) wait for all outstanding vector-memory operations.
+// The caller must wait for them itself (wait_vmem_all, then a barrier)
+// before reading the destination. The compiler's own waits stay correct:
+// vector-memory loads complete in issue order, so extra loads it does not
+// know about only make its waits longer. M0 is saved and restored; its write
+// needs one wait state before the load.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ void dma_lds16(const i32x4 &rsrc, int voffset, int soffset,
+                                          const void *lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(lds_base)), "v"(voffset), "s"(rsrc), "s"(soffset)
+      : "memory");
+}
+__device__ __forceinline__ void dma_lds4(const i32x4 &rsrc, int voffset, int soffset,
+                                         const void *lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(lds_base)), "v"(voffset), "s"(rsrc), "s"(soffset)
+      : "memory");
+}
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations, then s_barrier. Unlike __syncthreads() it does not wait for
 // outstanding vector-memory operations (direct-to-LDS loads of another

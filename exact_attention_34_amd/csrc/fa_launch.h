@@ -12,15 +12,18 @@ hipError_t launch_fwd(int dtype, int B, int H, int N, int d, const void *Q, cons
                       const void *V, float scale, int causal, void *O, float *LSE,
                       hipStream_t stream);
 
+// D = rowsum(dO o O), fp32 [B*H*N].
 hipError_t launch_bwd_preprocess(int dtype, int B, int H, int N, int d, const void *O,
-                                 const void *dO, float *Dvec, float *dQacc, hipStream_t stream);
+                                 const void *dO, float *Dvec, hipStream_t stream);
 
-hipError_t launch_bwd_main(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+// dK, dV (key blocks outer).
+hipError_t launch_bwd_dkdv(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
                            const void *V, const void *dO, const float *LSE, const float *Dvec,
-                           float scale, int causal, float *dQacc, void *dK, void *dV,
-                           hipStream_t stream);
+                           float scale, int causal, void *dK, void *dV, hipStream_t stream);
 
-hipError_t launch_bwd_dq_convert(int dtype, int B, int H, int N, int d, const float *dQacc,
-                                 float scale, void *dQ, hipStream_t stream);
+// dQ (query blocks outer).
+hipError_t launch_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                         const void *V, const void *dO, const float *LSE, const float *Dvec,
+                         float scale, int causal, void *dQ, hipStream_t stream);
 
 }  // namespace fa

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 /* element types */
 #define FA_F32 0
@@ -94,9 +94,8 @@ int fa_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
            void *stream);
 
 /*
- * Bytes of workspace fa_bwd needs: fp32 D [B, H, N] followed (at a 256-byte
- * aligned offset) by fp32 dQ accumulator [B, H, N, d]. Returns 0 for
- * arguments fa_bwd would reject.
+ * Bytes of workspace fa_bwd needs: fp32 D [B, H, N], rounded up to a
+ * multiple of 256. Returns 0 for arguments fa_bwd would reject.
  */
 size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d);
 
@@ -116,9 +115,9 @@ size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d);
  *   256-byte aligned, owned by the caller; overwritten (no need to clear it).
  * dtype: FA_F16 and FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED). P and dS
  * are rounded to dtype before the products that consume them; all sums are
- * fp32. dK and dV are deterministic; dQ is summed with fp32 atomics and may
- * differ in the last bits between runs.
- * Enqueues, in order: fa_bwd_preprocess, fa_bwd_main, fa_bwd_dq_convert.
+ * fp32. Deterministic: the same inputs give bit-identical dQ, dK and dV
+ * (every output element is summed by one thread in a fixed order).
+ * Enqueues, in order: fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq.
  */
 int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
            const void *V, const void *O, const void *dO, const float *LSE,
@@ -127,33 +126,40 @@ int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
 
 /*
  * The three stages of fa_bwd, for callers that schedule them separately.
+ * fa_bwd_dkdv and fa_bwd_dq only read what fa_bwd_preprocess wrote, so they
+ * may run in either order or concurrently (on two streams).
  *
  * fa_bwd_preprocess: Dvec_i = sum_k dO_ik * O_ik in fp32 ([FA] derivation
- *   page, part 5: computed once before the blocked loop, part 6) and
- *   dQacc = 0.  In: O, dO [B,H,N,d] dtype.  Out: Dvec [B,H,N] fp32,
- *   dQacc [B,H,N,d] fp32 (both caller-owned).
+ *   page, part 5: computed once before the blocked loop, part 6).
+ *   In: O, dO [B,H,N,d] dtype.  Out: Dvec [B,H,N] fp32 (caller-owned).
  */
 int fa_bwd_preprocess(int dtype, int B, int H, int N, int d, const void *O,
-                      const void *dO, float *Dvec, float *dQacc, void *stream);
+                      const void *dO, float *Dvec, void *stream);
 
 /*
- * fa_bwd_main: the blocked backward loop ([FA] section 3, part 4.2 and the
- *   derivation page, part 6) with the loops swapped: one workgroup owns a
- *   block of keys, keeps its dK and dV in registers, and walks the query
- *   tiles; dQ contributions (without the scale) are added atomically into
- *   dQacc, which must hold zeros (or a partial sum) on entry.
- *   In: Q, K, V, dO dtype; LSE, Dvec fp32.  Out: dK, dV dtype; dQacc fp32 +=.
+ * fa_bwd_dkdv: dK and dV by the blocked backward loop of [FA] (section 3,
+ *   part 4.2 and the derivation page, part 6): one workgroup owns a block
+ *   of keys, keeps its dK and dV in registers, and walks the query tiles,
+ *   recomputing P and dS for each.
+ *   In: Q, K, V, dO dtype; LSE, Dvec fp32.  Out: dK, dV dtype.
  */
-int fa_bwd_main(int dtype, int B, int H, int N, int d, const void *Q,
+int fa_bwd_dkdv(int dtype, int B, int H, int N, int d, const void *Q,
                 const void *K, const void *V, const void *dO, const float *LSE,
-                const float *Dvec, float scale, int causal, float *dQacc,
-                void *dK, void *dV, void *stream);
+                const float *Dvec, float scale, int causal, void *dK, void *dV,
+                void *stream);
 
 /*
- * fa_bwd_dq_convert: dQ = dtype(scale * dQacc), rounded to nearest even.
+ * fa_bwd_dq: dQ = scale * dS K ([FA] derivation page, parts 3-4) with the
+ *   loops the other way round: one workgroup owns a block of query rows,
+ *   keeps its dQ in registers, and walks the key tiles, recomputing P and
+ *   dS for each, so dQ is written once instead of being accumulated across
+ *   key blocks.
+ *   In: Q, K, V, dO dtype; LSE, Dvec fp32.  Out: dQ dtype.
  */
-int fa_bwd_dq_convert(int dtype, int B, int H, int N, int d,
-                      const float *dQacc, float scale, void *dQ, void *stream);
+int fa_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q,
+              const void *K, const void *V, const void *dO, const float *LSE,
+              const float *Dvec, float scale, int causal, void *dQ,
+              void *stream);
 
 #ifdef __cplusplus
 }

@@ -103,20 +103,24 @@ def test_bwd_rejects(L):
 
 
 def test_stage_entry_points_reject(L):
-    assert L.fa_bwd_preprocess(2, 1, 1, 0, 64, A, A, A, A, None) == INVALID
-    assert L.fa_bwd_preprocess(2, 1, 1, 8, 64, A, NUL, A, A, None) == INVALID
-    assert L.fa_bwd_main(1, 1, 1, 8, 64, A, A, A, A, A, A, 0.1, 3, A, A, A, None) == INVALID
-    assert L.fa_bwd_main(0, 1, 1, 8, 64, A, A, A, A, A, A, 0.1, 0, A, A, A, None) == UNSUP
-    assert L.fa_bwd_dq_convert(2, 1, 1, 8, 64, A, -0.5, A, None) == INVALID
-    assert L.fa_bwd_dq_convert(2, 1, 1, 8, 64, MIS, 0.5, A, None) == INVALID
+    assert L.fa_bwd_preprocess(2, 1, 1, 0, 64, A, A, A, None) == INVALID
+    assert L.fa_bwd_preprocess(2, 1, 1, 8, 64, A, NUL, A, None) == INVALID
+    assert L.fa_bwd_preprocess(0, 1, 1, 8, 64, A, A, A, None) == UNSUP
+    assert L.fa_bwd_dkdv(1, 1, 1, 8, 64, A, A, A, A, A, A, 0.1, 3, A, A, None) == INVALID
+    assert L.fa_bwd_dkdv(0, 1, 1, 8, 64, A, A, A, A, A, A, 0.1, 0, A, A, None) == UNSUP
+    assert L.fa_bwd_dkdv(2, 1, 1, 8, 64, A, A, A, A, A, A, 0.1, 0, MIS, A, None) == INVALID
+    assert L.fa_bwd_dkdv(2, 1, 1, 8, 64, A, A, A, A, A, NUL, 0.1, 0, A, A, None) == INVALID
+    assert L.fa_bwd_dq(2, 1, 1, 8, 64, A, A, A, A, A, A, -0.5, 0, A, None) == INVALID
+    assert L.fa_bwd_dq(2, 1, 1, 8, 96, A, A, A, A, A, A, 0.5, 0, A, None) == UNSUP
+    assert L.fa_bwd_dq(2, 1, 1, 8, 64, A, A, A, A, A, A, 0.5, 0, NUL, None) == INVALID
 
 
 @pytest.mark.parametrize("dtype,B,H,N,d", [(2, 1, 1, 1, 64), (1, 2, 3, 1000, 128),
                                           (2, 16, 32, 2048, 128)])
 def test_workspace_bytes(L, dtype, B, H, N, d):
-    """fp32 D [B,H,N] rounded up to 256 bytes, then fp32 dQ [B,H,N,d]."""
+    """fp32 D [B,H,N] rounded up to 256 bytes."""
     dbytes = -(-B * H * N * 4 // 256) * 256
-    assert L.fa_bwd_workspace_bytes(dtype, B, H, N, d) == dbytes + B * H * N * d * 4
+    assert L.fa_bwd_workspace_bytes(dtype, B, H, N, d) == dbytes
     assert L.fa_bwd_workspace_bytes(0, B, H, N, d) == 0     # fp32: no backward
     assert L.fa_bwd_workspace_bytes(dtype, B, H, N, 80) == 0
 
