@@ -165,12 +165,14 @@ __device__ __forceinline__ void load_lds16(const void *gptr, void *lds_base) {
 // stride 0, size in bytes (accesses at or past it read as zero), word 3 as
 // the gfx9 raw-buffer format.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+// Its words are wave-uniform by definition; readfirstlane keeps them in SGPRs
+// even where the compiler computes a uniform value with a vector instruction.
 __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
   const uint64_t a = (uint64_t)base;
   i32x4 r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
-  r[2] = (int)bytes;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
   r[3] = 0x00020000;
   return r;
 }
@@ -200,6 +202,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 __device__ __forceinline__ void dma_lds16(const i32x4 &rsrc, int voffset, int soffset,
                                           const void *lds_base) {
   uint32_t saved;
+  // Wave-uniform by contract; kept in SGPRs (the soffset field takes no
+  // literal).
+  soffset = __builtin_amdgcn_readfirstlane(soffset);
+  uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+  asm("" : "+s"(soffset), "+s"(m0v));
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
@@ -207,12 +214,17 @@ __device__ __forceinline__ void dma_lds16(const i32x4 &rsrc, int voffset, int so
       "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds_addr(lds_base)), "v"(voffset), "s"(rsrc), "s"(soffset)
+      : "s"(m0v), "v"(voffset), "s"(rsrc), "s"(soffset)
       : "memory");
 }
 __device__ __forceinline__ void dma_lds4(const i32x4 &rsrc, int voffset, int soffset,
                                          const void *lds_base) {
   uint32_t saved;
+  // Wave-uniform by contract; kept in SGPRs (the soffset field takes no
+  // literal).
+  soffset = __builtin_amdgcn_readfirstlane(soffset);
+  uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+  asm("" : "+s"(soffset), "+s"(m0v));
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
@@ -220,7 +232,7 @@ __device__ __forceinline__ void dma_lds4(const i32x4 &rsrc, int voffset, int sof
       "buffer_load_dword %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds_addr(lds_base)), "v"(voffset), "s"(rsrc), "s"(soffset)
+      : "s"(m0v), "v"(voffset), "s"(rsrc), "s"(soffset)
       : "memory");
 }
 // Workgroup barrier that orders LDS only: waits for this wave's LDS

@@ -22,9 +22,9 @@
 //     straight from registers; the V^T operand is read from the row-major V
 //     tile with transposing LDS reads (ds_read_b64_tr_b16).
 //   * K and V tiles are double-buffered in LDS (row-major, XOR-swizzled at
-//     16-byte granularity) and filled by direct global->LDS loads
-//     (global_load_lds_dwordx4): the loads of tile j+1 are issued right after
-//     the barrier that opens tile j and land while tile j is computed.
+//     16-byte granularity) and filled by direct buffer->LDS loads
+//     (buffer_load_dwordx4 ... lds): the loads of tile j+1 are issued right
+//     after the barrier that opens tile j and land while tile j is computed.
 // The fp32 variant is the same loop on v_mfma_f32_32x32x2_f32 with P kept in
 // fp32.
 
@@ -40,15 +40,17 @@ constexpr float kMaxSlack = 8.f;
 
 template <int D>
 struct FwdCfg {
-  static constexpr int kThreads = 256;       // 4 waves
-  static constexpr int BR = 128;             // query rows per workgroup, 32 per wave
-  static constexpr int BC = 64;              // keys per tile
-  static constexpr int CPR = D / 8;          // 16-byte chunks per row
-  static constexpr int TILE = BC * D;        // 16-bit elements per K or V tile
-  static constexpr int NCH = D / 16;         // 16-wide k chunks of q . k
-  static constexpr int NDT = D / 32;         // 32-wide output column tiles
-  static constexpr int LPW = BC * CPR / 256; // direct loads per wave per tile and tensor
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int BR = 32 * kWaves;           // query rows per workgroup, 32 per wave
+  static constexpr int BC = 64;                    // keys per tile
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int TILE = BC * D;              // 16-bit elements per K or V tile
+  static constexpr int NCH = D / 16;               // 16-wide k chunks of q . k
+  static constexpr int NDT = D / 32;               // 32-wide output column tiles
+  static constexpr int LPW = BC * CPR / kThreads;  // direct loads per wave per tile and tensor
   static constexpr int SH = (CPR == 16) ? 0 : 1;
+  static_assert(LPW >= 1, "every wave loads part of each tile");
 };
 
 // LDS tiles are unpadded and row-major at 16-byte-chunk granularity, with the
@@ -68,18 +70,23 @@ __device__ __forceinline__ int swz_v(int row) {
   return (4 * (row >> C::SH)) & (C::CPR - 4);
 }
 
+// The sweep is software-pipelined by one tile: while the softmax of tile j
+// runs on the vector ALUs, the matrix cores already compute the scores of
+// tile j + 1, so that each wave keeps both busy. K tiles are therefore
+// loaded two tiles ahead and V tiles one tile ahead.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
+__global__ __launch_bounds__(FwdCfg<D>::kThreads, 8 / FwdCfg<D>::kWaves) void fwd_b16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int N,
     int nqb, int total, float c2) {
   using C = FwdCfg<D>;
-  // Two buffers per tensor, named separately so that the compiler sees that
-  // the direct loads into one never alias the reads of the other.
-  __shared__ __attribute__((aligned(1024))) uint16_t K0[C::TILE], V0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t K1[C::TILE], V1[C::TILE];
+  // Two buffers per tensor, named separately so that the compiler can tell
+  // the direct loads into one from the reads of the other.
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[C::TILE], K1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[C::TILE], V1[C::TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int l32 = lane & 31, g = lane >> 5;
   const int tile = xcd_tile(blockIdx.x, total);
   const int bh = tile / nqb;
@@ -103,9 +110,7 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
 
   // Direct buffer -> LDS loads: instruction i of wave w fills LDS chunks
   // (w*LPW + i)*64 + lane; this lane fetches the global chunk that belongs
-  // there under the swizzle. Offsets are bytes within the (b, h) slice.
-  const i32x4 krs = make_rsrc(Kh, (uint32_t)N * D * 2);
-  const i32x4 vrs = make_rsrc(Vh, (uint32_t)N * D * 2);
+  // there under the swizzle (byte offset within the tile).
   int gk[C::LPW], gv[C::LPW];
 #pragma unroll
   for (int i = 0; i < C::LPW; ++i) {
@@ -114,26 +119,21 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
     gk[i] = 2 * (r * D + 8 * (sw ^ swz_k<D>(r)));
     gv[i] = 2 * (r * D + 8 * (sw ^ swz_v<D>(r)));
   }
-  auto issue = [&](uint16_t *Kb, uint16_t *Vb, int kt) __attribute__((always_inline)) {
+  // Buffer resource over the rows of tile kt that exist (below kend): the
+  // range check makes the loads of rows past them -- or of a whole tile past
+  // the last one -- write zeros, whose keys are masked.
+  auto tile_rsrc = [&](const uint16_t *src, int kt) __attribute__((always_inline)) {
     const int kb = kt * C::BC;
-    const int soff = kb * D * 2;
-    if (kb + C::BC <= N) {
-#pragma unroll
-      for (int i = 0; i < C::LPW; ++i) {
-        buffer_load_lds16(krs, gk[i], soff, Kb + (w * C::LPW + i) * 512);
-        buffer_load_lds16(vrs, gv[i], soff, Vb + (w * C::LPW + i) * 512);
-      }
-    } else {
-      // Tail tile: rows past N re-read row N - 1 (their keys are masked).
-#pragma unroll
-      for (int i = 0; i < C::LPW; ++i) {
-        const int r = ((w * C::LPW + i) * 64 + lane) / C::CPR;
-        const int shift = 2 * D * (min(kb + r, N - 1) - kb - r);  // <= 0
-        buffer_load_lds16(krs, gk[i] + shift, soff, Kb + (w * C::LPW + i) * 512);
-        buffer_load_lds16(vrs, gv[i] + shift, soff, Vb + (w * C::LPW + i) * 512);
-      }
-    }
+    const int rows = max(min(kend - kb, C::BC), 0);
+    return make_rsrc(src + (size_t)kb * D, (uint32_t)rows * D * 2);
   };
+  // Load i of this wave for tile kt of one tensor into the LDS tile dst.
+  auto dma = [&](const i32x4 &rs, const int (&go)[C::LPW], uint16_t *dst, int i)
+      __attribute__((always_inline)) {
+    buffer_load_lds16(rs, go[i], 0, dst + (w * C::LPW + i) * 512);
+  };
+  auto kbuf = [&](int b) { return b ? K1 : K0; };
+  auto vbuf = [&](int b) { return b ? V1 : V0; };
 
   // Per-lane operand offsets (elements). K, row-wise: row 32t + l%32,
   // chunk 2c + g. V, transposing: rows 4g + (l%16)/4 (+8 for the upper half
@@ -157,50 +157,90 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
   for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m_run = -INFINITY;  // running max of scaled scores (base-2 units)
+  float m_run = -INFINITY;  // running reference max of scaled scores (base-2 units)
   float l_run = 0.f;        // this lane's share of the running normaliser
 
-  // One K/V tile. MASK selects the variant for tiles that hold keys past N or
-  // past this wave's first query row (causal); other tiles skip the mask.
-  auto step = [&](const uint16_t *Ks, const uint16_t *Vs, int kb,
-                  auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    // Phase boundaries below are scheduling barriers: within a phase the
-    // compiler interleaves freely, across them it may not hoist operand
-    // reads (which would exceed the register budget of two waves per SIMD).
-    __builtin_amdgcn_sched_barrier(0);
-    // S^T = K Q^T, two 32-key subtiles; lane: query qrow, keys 8(r/4)+4g+r%4.
-    f32x16 s[2];
+  // S^T = K Q^T for one K tile, two 32-key subtiles; lane: query qrow, keys
+  // 8(r/4)+4g+r%4. MFMA c of subtile t is number 2c + t.
+  auto s_mfma = [&](f32x16 (&sx)[2], const uint16_t *Ks, int c) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
+      sx[t] = mfma32<T>(ld128(Ks + koff[c] + 32 * t * D), qreg[c], c == 0 ? kZero16 : sx[t]);
+  };
+  // P = 2^(s*c2 - m) for the 16 keys of chunk cc of subtile t (registers
+  // 8cc .. 8cc+7: keys 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3)),
+  // rounded to T in pairs -- the B operand of O~^T += V^T P^T. The row sum
+  // adds the fp32 values (the normaliser and LSE keep fp32 accuracy).
+  auto p_chunk = [&](const f32x16 &sx, int cc, float mb, float &psum)
+      __attribute__((always_inline)) {
+    u32x4 pp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
+    for (int h = 0; h < 4; ++h) {
+      const float p0 = fast_exp2(__builtin_fmaf(sx[8 * cc + 2 * h], c2, -mb));
+      const float p1 = fast_exp2(__builtin_fmaf(sx[8 * cc + 2 * h + 1], c2, -mb));
+      pp[h] = pack2<T>(p0, p1);
+      psum += p0 + p1;
+    }
+    return pp;
+  };
+  // O~^T += V^T P^T for chunk cc of subtile t; V^T takes the same keys for
+  // column 32dt + l%32 with two transposing reads.
+  auto pv_mfma = [&](const uint16_t *Vs, int t, int cc, const u32x4 &pp)
+      __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < C::NCH; ++c)
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      const uint16_t *src = Vs + voff[dt] + (32 * t + 16 * cc) * D;
+      o[dt] = mfma32<T>(cat(ld_tr16(src), ld_tr16(src + 8 * D)), pp, o[dt]);
+    }
+  };
+
+  // Vector instructions placed after each MFMA of phase A and of phase B
+  // (about the same vector work per tile for both head sizes, half the
+  // MFMAs for d = 64).
+  constexpr int kValuA = (D == 128) ? 6 : 14;
+  constexpr int kValuB = (D == 128) ? 4 : 7;
+  // MFMAs between two direct loads in phase A and in phase B.
+  constexpr int kDmaGapA = (2 * C::NCH - 2) / C::LPW;
+  constexpr int kDmaGapB = (4 * C::NDT) / C::LPW;
+
+  // One tile kt: s holds its scores (already issued), sn receives those of
+  // tile kt + 1 (from K buffer b ^ 1; past the last tile the result is
+  // unused). V of tile kt is in V buffer b.
+  auto step = [&](int kt, f32x16 (&s)[2], f32x16 (&sn)[2], int b) __attribute__((always_inline)) {
+    const int kb = kt * C::BC;
+    // Every wave's loads of K (kt + 1) and V (kt) have landed, and every wave
+    // is done with K buffer b (read for tile kt) and V buffer b ^ 1, which
+    // receive K (kt + 2) in phase A and V (kt + 1) in phase B.
+    wait_vmem_all();
+    __syncthreads();
+    const uint16_t *Kn = kbuf(b ^ 1), *Vs = vbuf(b);
+    const i32x4 krs = tile_rsrc(Kh, kt + 2), vrs = tile_rsrc(Vh, kt + 1);
+
+    // Phase A: the next tile's S MFMAs, with this tile's mask, row max,
+    // reference update and the first half of its exponentials in between.
+    __builtin_amdgcn_sched_barrier(0);
+    s_mfma(sn, Kn, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if ((kb + C::BC > N) || (CAUSAL && kb + C::BC - 1 > wq0)) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        s[t] = mfma32<T>(ld128(Ks + koff[c] + 32 * t * D), qreg[c], s[t]);
-    // Pipeline the operand reads two MFMA pairs ahead of their use.
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < C::NCH - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= N || (CAUSAL && key > qrow)) s[t][r] = -INFINITY;
+        }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) dma(krs, gk, kbuf(b), i);
+#pragma unroll
+    for (int c = 1; c < C::NCH; ++c) s_mfma(sn, Kn, c);
     // Row max of the raw scores (scale > 0 commutes with max).
     float mloc = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if constexpr (MASK) {
-          const int key = kb + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= N || (CAUSAL && key > qrow)) s[t][r] = -INFINITY;
-        }
-        mloc = fmaxf(mloc, s[t][r]);
-      }
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[t][r]);
     mloc = pair_max(mloc);
     // Reference max: moved only when the row max exceeds it by more than
     // kMaxSlack (base 2). Any reference gives the same O~ / l; keeping it
@@ -212,65 +252,72 @@ __global__ __launch_bounds__(256, 2) void fwd_b16_kernel(
       m_run = m_cand;
     }
     const float mb = (m_run == -INFINITY) ? 0.f : m_run;  // never form -inf - -inf
+    float psum = 0.f;
+    const u32x4 p00 = p_chunk(s[0], 0, mb, psum);
+    const u32x4 p01 = p_chunk(s[0], 1, mb, psum);
+    // Keep these exponentials in phase A (otherwise they sink past the
+    // rescale branch below).
+    asm volatile("" ::"v"(p00), "v"(p01), "v"(psum));
+    // Issue order: each MFMA with the K read of a later one and a few of the
+    // vector instructions, so the matrix core and the vector ALU overlap;
+    // the direct loads spread out so that no wave waits to issue them.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * C::NCH - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 2 * C::NCH - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuA, 0);
+      if (i % kDmaGapA == 0 && i / kDmaGapA < C::LPW)
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
-    // P = 2^(s*c2 - m), one FMA and one exp per score, rounded to T in pairs:
-    // 16-key chunk cc of subtile t = registers 8cc..8cc+7, i.e. keys
-    // 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3) -- the B operand of
-    // O~^T += V^T P^T. The A operand V^T takes the same keys for column
-    // 32dt + l%32 with two transposing reads. The row sum adds the fp32
-    // values (the normaliser and LSE keep fp32 accuracy).
-    float psum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        u32x4 pp;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[t][8 * cc + 2 * h], c2, -mb));
-          const float p1 = fast_exp2(__builtin_fmaf(s[t][8 * cc + 2 * h + 1], c2, -mb));
-          pp[h] = pack2<T>(p0, p1);
-          psum += p0 + p1;
-        }
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) {
-          const uint16_t *src = Vs + voff[dt] + (32 * t + 16 * cc) * D;
-          o[dt] = mfma32<T>(cat(ld_tr16(src), ld_tr16(src + 8 * D)), pp, o[dt]);
-        }
-      }
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase B: the P V MFMAs, with the second half of the exponentials.
+    pv_mfma(Vs, 0, 0, p00);
+    pv_mfma(Vs, 0, 1, p01);
+    const u32x4 p10 = p_chunk(s[1], 0, mb, psum);
+    pv_mfma(Vs, 1, 0, p10);
+    const u32x4 p11 = p_chunk(s[1], 1, mb, psum);
+    pv_mfma(Vs, 1, 1, p11);
     l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) dma(vrs, gv, vbuf(b ^ 1), i);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * C::NDT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 4 * C::NDT - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuB, 0);
+      if (i % kDmaGapB == 0 && i / kDmaGapB < C::LPW)
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto tile_step = [&](const uint16_t *Ks, const uint16_t *Vs, int kt) __attribute__((always_inline)) {
-    const int kb = kt * C::BC;
-    // Under the causal mask a wave whose rows all precede the tile skips it.
-    if (CAUSAL && kb > wq0 + 31) return;
-    if ((kb + C::BC > N) || (CAUSAL && kb + C::BC - 1 > wq0))
-      step(Ks, Vs, kb, std::true_type{});
-    else
-      step(Ks, Vs, kb, std::false_type{});
-  };
 
-  // Double-buffered sweep, unrolled by two so each half names its buffers:
-  // wait for this wave's loads of the tile, barrier (every wave's loads have
-  // landed and every wave is done with the other buffer), issue the next
-  // tile's loads into the other buffer, compute.
-  issue(K0, V0, 0);
+  f32x16 sa[2], sb[2];
+  {
+    const i32x4 k0rs = tile_rsrc(Kh, 0), k1rs = tile_rsrc(Kh, 1), v0rs = tile_rsrc(Vh, 0);
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      dma(k0rs, gk, K0, i);
+      dma(v0rs, gv, V0, i);
+      dma(k1rs, gk, K1, i);
+    }
+  }
+  wait_vmem_all();
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) s_mfma(sa, kbuf(0), c);
   for (int kt = 0; kt < ntiles; kt += 2) {
-    wait_vmem_all();
-    __syncthreads();
-    if (kt + 1 < ntiles) issue(K1, V1, kt + 1);
-    tile_step(K0, V0, kt);
+    step(kt, sa, sb, 0);
     if (kt + 1 >= ntiles) break;
-    wait_vmem_all();
-    __syncthreads();
-    if (kt + 2 < ntiles) issue(K0, V0, kt + 2);
-    tile_step(K1, V1, kt + 1);
+    step(kt + 1, sb, sa, 1);
   }
 
   // Epilogue: O = O~ / l, LSE = (m + log2 l) * ln 2.
