@@ -118,24 +118,35 @@ template <int D>
 struct DkdvCfg {
   static constexpr int kThreads = 512;               // 8 waves, two per SIMD
   static constexpr int KB = 128;                     // keys per workgroup, 32 per wave pair
-  static constexpr int BR = (D == 128) ? 64 : 128;   // query rows per step
-  static constexpr int NQW = BR / 64;                // 32-row query subtiles per wave
+  static constexpr int BR = 64;                      // query rows per step
+  static constexpr int NT = BR / 32;                 // 32-row query subtiles per step
   static constexpr int NCH = D / 16;
   static constexpr int NDT = D / 32;
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int QTILE = BR * D;               // 16-bit elements per Q or dO tile
-  static constexpr int LPW = BR * CPR / kThreads;    // direct loads per wave per tile and tensor
-  static_assert(LPW == 2, "two direct loads per wave per tile");
+  static constexpr int LPW = BR * CPR / (kThreads / 2);  // loads per role-0 wave per tile and tensor
+  static constexpr int PX = NT * 16 * 64;            // floats of P handed over per key slice
+  static constexpr int NBUF = 3;                     // query-tile buffers
+  static_assert(LPW >= 1, "every wave loads part of each tile");
 };
 
-// Per wave: a slice of 32 keys (column l % 32 of every S/P/dP/dS product)
-// and one half of each query tile. S and dP come out of the MFMA with one key
-// per lane and 16 query rows per lane, which is exactly the B-operand layout
-// of dV^T = dO^T P and dK^T = Q^T dS, so P and dS never leave registers; the
-// dO^T and Q^T operands are read from the row-major tiles with transposing
-// LDS reads. The two waves of a key slice sum their dK, dV partials through
-// LDS at the end. Query tiles (Q, dO, LSE, D) are double-buffered and filled
-// by direct buffer -> LDS loads issued one tile ahead.
+// The eight waves form four pairs, one per SIMD; a pair owns a slice of 32
+// keys (column l % 32 of every S/P/dP/dS product) and splits the work by
+// role:
+//   * role 0 keeps the slice's K rows in VGPRs (B operand of S = Q K^T),
+//     forms P = exp(scale S - LSE), hands P to its partner through LDS and
+//     accumulates dV^T += dO^T P;
+//   * role 1 keeps the V rows in VGPRs (B operand of dP = dO V^T), forms
+//     dS = P o (dP - D) and accumulates dK^T += Q^T dS.
+// Each product reads one operand from LDS; P and dS come out of the MFMA in
+// the B-operand layout of the dV / dK products (one key per lane, 16 query
+// rows per lane), and dO^T / Q^T come from transposing reads of the
+// row-major tiles. Role 1 forms dK one tile late, so that in the first half
+// of a step (before P is handed over) it runs the MFMAs of the previous
+// tile's dK and of this tile's dP while role 0 computes exponentials, and in
+// the second half its dS arithmetic runs beside role 0's dV MFMAs. Query
+// tiles (Q, dO, LSE, D) are triple-buffered (the tile being read, the
+// previous one for role 1's dK, and the next one being loaded).
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
@@ -143,19 +154,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dK,
     uint16_t *__restrict__ dV, int N, int nkb, int total, float c2, float scale) {
   using C = DkdvCfg<D>;
-  // Double buffers for the query tiles: buffer b holds Q at
-  // qo + 2*b*QTILE, dO right after it, and LSE, D rows at lv + 2*b*BR. Then
-  // the key block's K and V.
-  __shared__ __attribute__((aligned(1024))) uint16_t qo[4 * C::QTILE];
-  __shared__ __attribute__((aligned(256))) float lv[4 * C::BR];
-  __shared__ __attribute__((aligned(1024))) uint16_t Kst[C::KB * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vst[C::KB * D];
+  constexpr int NT = C::NT;
+  // Query-tile buffers: buffer b holds Q at qo + 2*b*QTILE, dO right after
+  // it, and LSE, D rows at lv + 2*b*BR; then the P hand-over area, PX floats
+  // per key slice.
+  __shared__ __attribute__((aligned(1024))) uint16_t qo[2 * C::NBUF * C::QTILE];
+  __shared__ __attribute__((aligned(256))) float lv[2 * C::NBUF * C::BR];
+  __shared__ __attribute__((aligned(1024))) float px[4 * C::PX];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int l32 = lane & 31, g = lane >> 5;
-  const int ks = w & 3;   // key slice: keys 32 ks .. +31 of the block
-  const int qh = w >> 2;  // query half: subtiles qh*NQW .. +NQW-1 of each query tile
+  const int ks = w & 3;     // key slice: keys 32 ks .. +31 of the block
+  const int role = w >> 2;  // 0: S, P, dV; 1: dP, dS, dK
   const int tile = xcd_tile(blockIdx.x, total);
   const int bh = tile / nkb;
   const int kb = tile - bh * nkb;
@@ -163,260 +174,226 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int wk0 = k0 + 32 * ks;  // first key of this wave
   const int mykey = wk0 + l32;   // key of this lane's S/P column
   const size_t base = (size_t)bh * N * D;
-  const uint16_t *Qh = Q + base, *Kh = K + base, *Vh = V + base, *dOh = dO + base;
+  const uint16_t *Qh = Q + base, *dOh = dO + base;
 
-  // K and V of the key block into LDS; keys past N read row N - 1 (masked).
-  for (int c = tid; c < C::KB * C::CPR; c += C::kThreads) {
-    const int row = c / C::CPR, ch = c % C::CPR;
-    const int key = min(k0 + row, N - 1);
-    const int pos = row * D + 8 * (ch ^ swz<D>(row));
-    st128(Kst + pos, ld128(Kh + (size_t)key * D + 8 * ch));
-    st128(Vst + pos, ld128(Vh + (size_t)key * D + 8 * ch));
+  // This slice's K (role 0) or V (role 1) rows as the B operand: lane l holds
+  // key mykey, 8 consecutive columns 16c + 8g .. per chunk c. Keys past N
+  // read row N - 1 (masked).
+  u32x4 kv[C::NCH];
+  {
+    const uint16_t *src = (role == 0 ? K : V) + base + (size_t)min(mykey, N - 1) * D;
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) kv[c] = ld128(src + 16 * c + 8 * g);
   }
 
   const int nq = (N + C::BR - 1) / C::BR;
   const int it0 = CAUSAL ? k0 / C::BR : 0;  // earlier queries see none of these keys
 
-  // Direct buffer -> LDS loads of a query tile: instruction i of wave w fills
-  // LDS chunks (w*LPW + i)*64 + lane with the global chunk the swizzle puts
-  // there. Waves 0 .. 2*BR/64-1 also load 64 LSE or D values each. Rows
-  // past N re-read row N - 1 and are masked.
-  const i32x4 qrs = make_rsrc(Qh, (uint32_t)N * D * 2);
-  const i32x4 ors = make_rsrc(dOh, (uint32_t)N * D * 2);
-  const i32x4 lrs = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
-  const i32x4 drs = make_rsrc(Dvec + (size_t)bh * N, (uint32_t)N * 4);
-  constexpr int kVecParts = C::BR / 64;
-  int gq[C::LPW], grow[C::LPW];
+  // Direct buffer -> LDS loads of a query tile, issued by the role-0 waves
+  // (which have slack while their partners finish dK and dP): instruction i
+  // of wave w fills LDS chunks (w*LPW + i)*64 + lane with the global chunk
+  // the swizzle puts there. Waves 0 .. 2*BR/64-1 also load 64 LSE or D
+  // values each. The buffer resources cover the rows that exist; rows past
+  // N read as zero (and are masked).
+  int gq[C::LPW];
 #pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    const int p = (w * C::LPW + i) * 64 + lane;
-    grow[i] = p / C::CPR;
-    gq[i] = src_of_chunk<D>(p);
-  }
+  for (int i = 0; i < C::LPW; ++i) gq[i] = src_of_chunk<D>((w * C::LPW + i) * 64 + lane);
+  constexpr int kVecParts = C::BR / 64;
   auto issue = [&](int b, int it) __attribute__((always_inline)) {
     uint16_t *Qb = qo + 2 * b * C::QTILE, *Ob = Qb + C::QTILE;
     const int q0 = it * C::BR;
-    const int soff = q0 * D * 2;
-    if (q0 + C::BR <= N) {
+    const int rows = min(N - q0, C::BR);
+    const i32x4 qrs = make_rsrc(Qh + (size_t)q0 * D, (uint32_t)rows * D * 2);
+    const i32x4 ors = make_rsrc(dOh + (size_t)q0 * D, (uint32_t)rows * D * 2);
 #pragma unroll
-      for (int i = 0; i < C::LPW; ++i) {
-        dma_lds16(qrs, gq[i], soff, Qb + (w * C::LPW + i) * 512);
-        dma_lds16(ors, gq[i], soff, Ob + (w * C::LPW + i) * 512);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::LPW; ++i) {
-        const int shift = 2 * D * (min(q0 + grow[i], N - 1) - q0 - grow[i]);  // <= 0
-        dma_lds16(qrs, gq[i] + shift, soff, Qb + (w * C::LPW + i) * 512);
-        dma_lds16(ors, gq[i] + shift, soff, Ob + (w * C::LPW + i) * 512);
-      }
+    for (int i = 0; i < C::LPW; ++i) {
+      dma_lds16(qrs, gq[i], 0, Qb + (w * C::LPW + i) * 512);
+      dma_lds16(ors, gq[i], 0, Ob + (w * C::LPW + i) * 512);
     }
     if (w < 2 * kVecParts) {
       const int vec = w / kVecParts, part = w % kVecParts;
-      const int voff = 4 * (min(q0 + 64 * part + lane, N - 1) - q0);
-      dma_lds4(vec == 0 ? lrs : drs, voff, 4 * q0, lv + 2 * b * C::BR + vec * C::BR + 64 * part);
+      const i32x4 vrs =
+          make_rsrc((vec == 0 ? LSE : Dvec) + (size_t)bh * N + q0, (uint32_t)rows * 4);
+      dma_lds4(vrs, 4 * (64 * part + lane), 0, lv + 2 * b * C::BR + vec * C::BR + 64 * part);
     }
   };
 
-  // Row-wise reads: this wave's keys 32 ks + l%32 of the K and V tiles, and
-  // its query rows (subtiles qh*NQW ..) of the Q and dO tiles.
+  // Row-wise reads (row 32t + l%32 of a tile, chunk 2c + g) and transposing
+  // reads (rows 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3) of subtile t:
+  // the P / dS register layout), as per-lane bases XOR-ed with constants.
   const int rb = row_base<D>(lane);
-  const int kb_off = rb | (64 * D * ks);
-  const int qb_off = rb | (64 * D * C::NQW * qh);
-  // Q^T / dO^T operands: rows 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3)
-  // of a 32-row subtile (the P / dS register layout), in this wave's subtiles.
-  const int tb1 = tr_base<D>(4 * g, lane) | (64 * D * C::NQW * qh);
-  const int tb2 = tr_base<D>(8 + 4 * g, lane) | (64 * D * C::NQW * qh);
+  const int tb1 = tr_base<D>(4 * g, lane), tb2 = tr_base<D>(8 + 4 * g, lane);
+  float *pxs = px + ks * C::PX;  // this slice's P hand-over area
 
-  // dK^T and dV^T partial sums (this wave's query half): column = key
-  // (l % 32), rows = d.
-  f32x16 dk[C::NDT], dv[C::NDT];
+  // Issue pattern of a phase of kM MFMAs, each fed by kR LDS reads issued
+  // kA MFMAs ahead (LDS latency under load exceeds a few MFMAs).
+  auto pipeline = [&](auto km_tag, auto kr_tag, auto ka_tag) __attribute__((always_inline)) {
+    constexpr int kM = decltype(km_tag)::value, kR = decltype(kr_tag)::value;
+    constexpr int kA = decltype(ka_tag)::value;
+    __builtin_amdgcn_sched_group_barrier(0x100, kA * kR, 0);
 #pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[dt][r] = 0.f;
-      dv[dt][r] = 0.f;
-    }
-
-  // Scheduling pattern of a product phase of kM MFMAs fed by two transposing
-  // reads each: reads two MFMAs ahead, then the phase ends.
-  auto tr_pipeline = [&](auto km_tag) __attribute__((always_inline)) {
-    constexpr int kM = decltype(km_tag)::value;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < kM - 2; ++i) {
+    for (int i = 0; i < kM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (i < kM - kA) __builtin_amdgcn_sched_group_barrier(0x100, kR, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  using KM = std::integral_constant<int, 2 * C::NQW * C::NDT>;
+  using KR = std::integral_constant<int, NT * C::NCH>;      // MFMAs of a row-wise product
+  using KT = std::integral_constant<int, 2 * NT * C::NDT>;  // MFMAs of a transposed product
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using I6 = std::integral_constant<int, 6>;
 
-  // This wave's part of one query tile. need_mask: the rows hold rows past N,
-  // keys past N, or (causal) keys after some row; masked scores become -inf,
-  // so P and dS are exactly 0 there. The mask is a VALU-only branch, so every
-  // MFMA accumulation runs on one code path.
-  auto step = [&](const uint16_t *Qs, const uint16_t *Os, const float *Lb, int it)
+  // One product with an operand read row-wise from a tile: acc[t] = Σ_c
+  // tile rows (32t + l%32, chunk c) x kv[c].
+  auto rows_x_kv = [&](f32x16 (&acc)[NT], const uint16_t *tile) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int c = 0; c < C::NCH; ++c)
+        acc[t] = mfma32<T>(ld128(at(tile + 32 * D * t, rb ^ (32 * c))), kv[c],
+                           c == 0 ? kZero16 : acc[t]);
+  };
+  // acc^T += tile^T x B for B in the P / dS layout (pb[t][cc]).
+  auto tr_x_b = [&](f32x16 (&acc)[C::NDT], const uint16_t *tile, const u32x4 (&pb)[NT][2])
       __attribute__((always_inline)) {
-    const int q0 = it * C::BR;
-    const int q0w = q0 + 32 * C::NQW * qh;  // first query row of this wave
-    const bool need_mask =
-        (q0w + 32 * C::NQW > N) || (wk0 + 32 > N) || (CAUSAL && wk0 + 31 > q0w);
-    __builtin_amdgcn_sched_barrier(0);
-    // S = Q K^T and dP = dO V^T: column = key, rows 8(r/4) + 4g + r%4.
-    f32x16 s[C::NQW], dp[C::NQW];
 #pragma unroll
-    for (int t = 0; t < C::NQW; ++t) {
-#pragma unroll
-      for (int c = 0; c < C::NCH; ++c) {
-        s[t] = mfma32<T>(ld128(at(Qs + 32 * D * t, qb_off ^ (32 * c))),
-                         ld128(at(Kst, kb_off ^ (32 * c))), c == 0 ? kZero16 : s[t]);
-        dp[t] = mfma32<T>(ld128(at(Os + 32 * D * t, qb_off ^ (32 * c))),
-                          ld128(at(Vst, kb_off ^ (32 * c))), c == 0 ? kZero16 : dp[t]);
-      }
-    }
-    // Operand reads two MFMAs ahead of their use (bounded register use).
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * C::NQW * C::NCH - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (need_mask) {
-#pragma unroll
-      for (int t = 0; t < C::NQW; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = q0 + 32 * (qh * C::NQW + t) + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (q >= N || mykey >= N || (CAUSAL && mykey > q)) s[t][r] = -INFINITY;
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // P = 2^(S*scale*log2e - LSE*log2e); rows j = 0..3 of group i are
-    // consecutive in LDS, read as one 16-byte word.
-#pragma unroll
-    for (int t = 0; t < C::NQW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 lse = *(const f32x4 *)(Lb + 32 * (qh * C::NQW + t) + 8 * i + 4 * g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * i + j;
-          s[t][r] = fast_exp2(__builtin_fmaf(s[t][r], c2, -lse[j] * kLog2e));
-        }
-      }
-    // dV^T += dO^T P
-    u32x4 pk[C::NQW][2];
-#pragma unroll
-    for (int t = 0; t < C::NQW; ++t)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          pk[t][cc][h] = pack2<T>(s[t][8 * cc + 2 * h], s[t][8 * cc + 2 * h + 1]);
-#pragma unroll
-    for (int t = 0; t < C::NQW; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
-          const uint16_t *src = Os + (32 * t + 16 * cc) * D;
-          dv[dt] = mfma32<T>(
+          const uint16_t *src = tile + (32 * t + 16 * cc) * D;
+          acc[dt] = mfma32<T>(
               cat(ld_tr16(at(src, tb1 ^ (64 * dt))), ld_tr16(at(src, tb2 ^ (64 * dt)))),
-              pk[t][cc], dv[dt]);
+              pb[t][cc], acc[dt]);
         }
-    tr_pipeline(KM{});
-    // dS = P o (dP - D)
+  };
+  auto pack_b = [&](const f32x16 (&x)[NT], u32x4 (&pb)[NT][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < C::NQW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 dd = *(const f32x4 *)(Lb + C::BR + 32 * (qh * C::NQW + t) + 8 * i + 4 * g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dp[t][4 * i + j] = s[t][4 * i + j] * (dp[t][4 * i + j] - dd[j]);
-      }
-    // dK^T += Q^T dS
-#pragma unroll
-    for (int t = 0; t < C::NQW; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int h = 0; h < 4; ++h)
-          pk[t][cc][h] = pack2<T>(dp[t][8 * cc + 2 * h], dp[t][8 * cc + 2 * h + 1]);
-#pragma unroll
-    for (int t = 0; t < C::NQW; ++t)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) {
-          const uint16_t *src = Qs + (32 * t + 16 * cc) * D;
-          dk[dt] = mfma32<T>(
-              cat(ld_tr16(at(src, tb1 ^ (64 * dt))), ld_tr16(at(src, tb2 ^ (64 * dt)))),
-              pk[t][cc], dk[dt]);
-        }
-    tr_pipeline(KM{});
+          pb[t][cc][h] = pack2<T>(x[t][8 * cc + 2 * h], x[t][8 * cc + 2 * h + 1]);
   };
 
-  // Double-buffered sweep over the query tiles: wait for this wave's loads,
-  // barrier (every wave's loads landed; every wave is done with the other
-  // buffer), issue the next tile's loads into the other buffer, compute.
-  __syncthreads();  // K and V staged
-  if (it0 < nq) issue(0, it0);
-  for (int it = it0; it < nq; ++it) {
-    const int b = (it - it0) & 1;
+  // Tile `it` (in buffer b = (it - it0) % 3): wait for this wave's loads,
+  // barrier (every wave's loads landed; every wave is done with tile it - 2
+  // and with the P of the previous tile). The next tile's loads go into the
+  // buffer of tile it - 2 (role 0, later in the step).
+  auto top = [&]() __attribute__((always_inline)) {
     wait_vmem_all();
     __syncthreads();
-    if (it + 1 < nq) issue(b ^ 1, it + 1);
-    const uint16_t *Qs = qo + 2 * b * C::QTILE;
-    step(Qs, Qs + C::QTILE, lv + 2 * b * C::BR, it);
+  };
+  // rows of subtile t, register r: 8(r/4) + 4g + r%4; LSE and D of rows
+  // 8i + 4g + (0..3) are consecutive in LDS, read as one 16-byte word.
+  auto vec4 = [&](const float *Lb, int off, int t, int i) __attribute__((always_inline)) {
+    return *(const f32x4 *)(Lb + off + 32 * t + 8 * i + 4 * g);
+  };
+
+  f32x16 acc[C::NDT];  // dV^T (role 0) or dK^T (role 1): column = key, rows = d
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) acc[dt] = kZero16;
+
+  if (role == 0 && it0 < nq) issue(0, it0);
+  if (role == 0) {
+    for (int it = it0, b = 0; it < nq; ++it, b = (b == 2 ? 0 : b + 1)) {
+      top();
+      const uint16_t *Qs = qo + 2 * b * C::QTILE, *Os = Qs + C::QTILE;
+      const float *Lb = lv + 2 * b * C::BR;
+      const int q0 = it * C::BR;
+      const bool need_mask = (q0 + C::BR > N) || (wk0 + 32 > N) || (CAUSAL && wk0 + 31 > q0);
+      f32x4 lse[NT][4];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lse[t][i] = vec4(Lb, 0, t, i);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 s[NT];
+      rows_x_kv(s, Qs);  // S = Q K^T
+      pipeline(KR{}, I1{}, I6{});
+      if (need_mask) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int q = q0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (q >= N || mykey >= N || (CAUSAL && mykey > q)) s[t][r] = -INFINITY;
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // P = 2^(S*scale*log2e - LSE*log2e), handed over in fp32 (lane-major
+      // 16-byte groups), and rounded to T for dV.
+      u32x4 pp[NT][2];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 p;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            p[j] = fast_exp2(__builtin_fmaf(s[t][4 * i + j], c2, -lse[t][i][j] * kLog2e));
+          *(f32x4 *)(pxs + ((t * 4 + i) * 64 + lane) * 4) = p;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s[t][4 * i + j] = p[j];
+        }
+      pack_b(s, pp);
+      if (it + 1 < nq) issue(b == 2 ? 0 : b + 1, it + 1);
+      barrier_lds();  // P visible to the partner
+      tr_x_b(acc, Os, pp);  // dV^T += dO^T P
+      pipeline(KT{}, I2{}, I4{});
+    }
+  } else {
+    u32x4 pd[NT][2];  // dS of the previous tile, rounded to T
+    const uint16_t *Qprev = qo;
+    for (int it = it0, b = 0; it < nq; ++it, b = (b == 2 ? 0 : b + 1)) {
+      top();
+      const uint16_t *Qs = qo + 2 * b * C::QTILE, *Os = Qs + C::QTILE;
+      const float *Lb = lv + 2 * b * C::BR;
+      if (it > it0) {
+        tr_x_b(acc, Qprev, pd);  // dK^T += Q^T dS of the previous tile
+        pipeline(KT{}, I2{}, I4{});
+      }
+      f32x16 dp[NT];
+      rows_x_kv(dp, Os);  // dP = dO V^T
+      pipeline(KR{}, I1{}, I6{});
+      barrier_lds();  // the partner's P is in LDS
+      // dS = P o (dP - D), rounded to T.
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 p = *(const f32x4 *)(pxs + ((t * 4 + i) * 64 + lane) * 4);
+          const f32x4 dd = vec4(Lb, C::BR, t, i);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dp[t][4 * i + j] = p[j] * (dp[t][4 * i + j] - dd[j]);
+        }
+      pack_b(dp, pd);
+      __builtin_amdgcn_sched_barrier(0);
+      Qprev = Qs;
+    }
+    if (it0 < nq) {
+      tr_x_b(acc, Qprev, pd);  // dK^T += Q^T dS of the last tile
+      pipeline(KT{}, I2{}, I4{});
+    }
   }
 
-  // Sum the two query halves' partial dK, dV (waves ks and ks + 4) through
-  // LDS: the second half writes its partials lane-major into free tiles
-  // (NDT * 16 * 64 floats each: a quarter of the query buffers, or half of K
-  // or V).
-  __syncthreads();
-  constexpr int kPart = C::NDT * 16 * 64;
-  static_assert(4 * C::QTILE * 2 >= 4 * kPart * 4 && C::KB * D * 2 >= 2 * kPart * 4,
-                "partials fit in the freed tiles");
-  float *xk = ks < 2 ? (float *)qo + 2 * ks * kPart : ks == 2 ? (float *)Kst : (float *)Vst;
-  float *xv = xk + kPart;
-  if (qh == 1) {
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        xk[(dt * 16 + r) * 64 + lane] = dk[dt][r];
-        xv[(dt * 16 + r) * 64 + lane] = dv[dt][r];
-      }
-  }
-  __syncthreads();
-  if (qh == 0 && mykey < N) {
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dk[dt][r] += xk[(dt * 16 + r) * 64 + lane];
-        dv[dt][r] += xv[(dt * 16 + r) * 64 + lane];
-      }
-    // dK = scale * dK, dV; lane holds 4 consecutive columns per row.
-    uint16_t *dKrow = dK + base + (size_t)mykey * D;
-    uint16_t *dVrow = dV + base + (size_t)mykey * D;
+  // dK = scale * dK (role 1), dV (role 0); lane holds 4 consecutive columns
+  // per row.
+  if (mykey < N) {
+    uint16_t *row = (role == 0 ? dV : dK) + base + (size_t)mykey * D;
+    const float f = role == 0 ? 1.f : scale;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        u32x2 a, b;
-        a[0] = pack2<T>(dk[dt][4 * i] * scale, dk[dt][4 * i + 1] * scale);
-        a[1] = pack2<T>(dk[dt][4 * i + 2] * scale, dk[dt][4 * i + 3] * scale);
-        b[0] = pack2<T>(dv[dt][4 * i], dv[dt][4 * i + 1]);
-        b[1] = pack2<T>(dv[dt][4 * i + 2], dv[dt][4 * i + 3]);
-        *(u32x2 *)(dKrow + 32 * dt + 8 * i + 4 * g) = a;
-        *(u32x2 *)(dVrow + 32 * dt + 8 * i + 4 * g) = b;
+        u32x2 a;
+        a[0] = pack2<T>(acc[dt][4 * i] * f, acc[dt][4 * i + 1] * f);
+        a[1] = pack2<T>(acc[dt][4 * i + 2] * f, acc[dt][4 * i + 3] * f);
+        *(u32x2 *)(row + 32 * dt + 8 * i + 4 * g) = a;
       }
   }
 }

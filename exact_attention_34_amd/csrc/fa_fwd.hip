@@ -266,7 +266,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 8 / FwdCfg<D>::kWaves) void fw
     for (int i = 0; i < 2 * C::NCH - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < 2 * C::NCH - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuA, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, kValuA, 0);
       if (i % kDmaGapA == 0 && i / kDmaGapA < C::LPW)
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     }
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 8 / FwdCfg<D>::kWaves) void fw
     for (int i = 0; i < 4 * C::NDT; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < 4 * C::NDT - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, kValuB, 0);
       if (i % kDmaGapB == 0 && i / kDmaGapB < C::LPW)
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     }
