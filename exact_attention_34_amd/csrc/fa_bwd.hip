@@ -148,7 +148,7 @@ struct DkdvCfg {
 // tiles (Q, dO, LSE, D) are triple-buffered (the tile being read, the
 // previous one for role 1's dK, and the next one being loaded).
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dK,

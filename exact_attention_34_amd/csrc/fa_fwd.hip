@@ -41,9 +41,11 @@ constexpr float kMaxSlack = 8.f;
 template <int D>
 struct FwdCfg {
   static constexpr int kWaves = 4;
+  static constexpr int kWavesPerSimd = 2;          // resident waves per SIMD (register budget)
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BR = 32 * kWaves;           // query rows per workgroup, 32 per wave
   static constexpr int BC = 64;                    // keys per tile
+  static constexpr int NT = BC / 32;               // 32-key subtiles per tile
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
   static constexpr int TILE = BC * D;              // 16-bit elements per K or V tile
   static constexpr int NCH = D / 16;               // 16-wide k chunks of q . k
@@ -75,7 +77,7 @@ __device__ __forceinline__ int swz_v(int row) {
 // tile j + 1, so that each wave keeps both busy. K tiles are therefore
 // loaded two tiles ahead and V tiles one tile ahead.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(FwdCfg<D>::kThreads, 8 / FwdCfg<D>::kWaves) void fwd_b16_kernel(
+__global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void fwd_b16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int N,
     int nqb, int total, float c2) {
@@ -160,11 +162,12 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 8 / FwdCfg<D>::kWaves) void fw
   float m_run = -INFINITY;  // running reference max of scaled scores (base-2 units)
   float l_run = 0.f;        // this lane's share of the running normaliser
 
-  // S^T = K Q^T for one K tile, two 32-key subtiles; lane: query qrow, keys
-  // 8(r/4)+4g+r%4. MFMA c of subtile t is number 2c + t.
-  auto s_mfma = [&](f32x16 (&sx)[2], const uint16_t *Ks, int c) __attribute__((always_inline)) {
+  constexpr int NT = C::NT;
+  // S^T = K Q^T for one K tile, NT 32-key subtiles; lane: query qrow, keys
+  // 8(r/4)+4g+r%4. MFMA c of subtile t is number NT c + t.
+  auto s_mfma = [&](f32x16 (&sx)[NT], const uint16_t *Ks, int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NT; ++t)
       sx[t] = mfma32<T>(ld128(Ks + koff[c] + 32 * t * D), qreg[c], c == 0 ? kZero16 : sx[t]);
   };
   // P = 2^(s*c2 - m) for the 16 keys of chunk cc of subtile t (registers
@@ -199,14 +202,19 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 8 / FwdCfg<D>::kWaves) void fw
   // MFMAs for d = 64).
   constexpr int kValuA = (D == 128) ? 6 : 14;
   constexpr int kValuB = (D == 128) ? 4 : 7;
-  // MFMAs between two direct loads in phase A and in phase B.
-  constexpr int kDmaGapA = (2 * C::NCH - 2) / C::LPW;
-  constexpr int kDmaGapB = (4 * C::NDT) / C::LPW;
+  // MFMAs of phase A (after the first NT) and of phase B; MFMAs between two
+  // direct loads in each.
+  constexpr int kMfmaA = NT * C::NCH - NT, kMfmaB = 2 * NT * C::NDT;
+  constexpr int kDmaGapA = kMfmaA / C::LPW;
+  constexpr int kDmaGapB = kMfmaB / C::LPW;
+  // Exponential chunks (subtile t, 16-key chunk cc) in phase A: the first
+  // half; the rest in phase B.
+  constexpr int kChunksA = NT;
 
   // One tile kt: s holds its scores (already issued), sn receives those of
   // tile kt + 1 (from K buffer b ^ 1; past the last tile the result is
   // unused). V of tile kt is in V buffer b.
-  auto step = [&](int kt, f32x16 (&s)[2], f32x16 (&sn)[2], int b) __attribute__((always_inline)) {
+  auto step = [&](int kt, f32x16 (&s)[NT], f32x16 (&sn)[NT], int b) __attribute__((always_inline)) {
     const int kb = kt * C::BC;
     // Every wave's loads of K (kt + 1) and V (kt) have landed, and every wave
     // is done with K buffer b (read for tile kt) and V buffer b ^ 1, which
@@ -223,7 +231,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 8 / FwdCfg<D>::kWaves) void fw
     __builtin_amdgcn_sched_barrier(0);
     if ((kb + C::BC > N) || (CAUSAL && kb + C::BC - 1 > wq0)) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -238,7 +246,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 8 / FwdCfg<D>::kWaves) void fw
     // Row max of the raw scores (scale > 0 commutes with max).
     float mloc = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[t][r]);
     mloc = pair_max(mloc);
@@ -253,19 +261,23 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 8 / FwdCfg<D>::kWaves) void fw
     }
     const float mb = (m_run == -INFINITY) ? 0.f : m_run;  // never form -inf - -inf
     float psum = 0.f;
-    const u32x4 p00 = p_chunk(s[0], 0, mb, psum);
-    const u32x4 p01 = p_chunk(s[0], 1, mb, psum);
-    // Keep these exponentials in phase A (otherwise they sink past the
-    // rescale branch below).
-    asm volatile("" ::"v"(p00), "v"(p01), "v"(psum));
+    u32x4 pch[2 * NT];  // chunk 2t + cc
+#pragma unroll
+    for (int k = 0; k < kChunksA; ++k) {
+      pch[k] = p_chunk(s[k / 2], k % 2, mb, psum);
+      // Keep these exponentials in phase A (otherwise they sink past the
+      // rescale branch below).
+      asm volatile("" ::"v"(pch[k]));
+    }
+    asm volatile("" ::"v"(psum));
     // Issue order: each MFMA with the K read of a later one and a few of the
     // vector instructions, so the matrix core and the vector ALU overlap;
     // the direct loads spread out so that no wave waits to issue them.
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * C::NCH - 2; ++i) {
+    for (int i = 0; i < kMfmaA; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < 2 * C::NCH - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < kMfmaA - 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x402, kValuA, 0);
       if (i % kDmaGapA == 0 && i / kDmaGapA < C::LPW)
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
@@ -279,20 +291,19 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 8 / FwdCfg<D>::kWaves) void fw
     }
     __builtin_amdgcn_sched_barrier(0);
     // Phase B: the P V MFMAs, with the second half of the exponentials.
-    pv_mfma(Vs, 0, 0, p00);
-    pv_mfma(Vs, 0, 1, p01);
-    const u32x4 p10 = p_chunk(s[1], 0, mb, psum);
-    pv_mfma(Vs, 1, 0, p10);
-    const u32x4 p11 = p_chunk(s[1], 1, mb, psum);
-    pv_mfma(Vs, 1, 1, p11);
+#pragma unroll
+    for (int k = 0; k < 2 * NT; ++k) {
+      if (k >= kChunksA) pch[k] = p_chunk(s[k / 2], k % 2, mb, psum);
+      pv_mfma(Vs, k / 2, k % 2, pch[k]);
+    }
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) dma(vrs, gv, vbuf(b ^ 1), i);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 4 * C::NDT; ++i) {
+    for (int i = 0; i < kMfmaB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < 4 * C::NDT - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (i < kMfmaB - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x402, kValuB, 0);
       if (i % kDmaGapB == 0 && i / kDmaGapB < C::LPW)
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
@@ -300,7 +311,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 8 / FwdCfg<D>::kWaves) void fw
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  f32x16 sa[2], sb[2];
+  f32x16 sa[NT], sb[NT];
   {
     const i32x4 k0rs = tile_rsrc(Kh, 0), k1rs = tile_rsrc(Kh, 1), v0rs = tile_rsrc(Vh, 0);
 #pragma unroll
