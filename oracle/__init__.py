@@ -41,6 +41,9 @@ def _load():
     lib.oracle_bwd.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_lse_merge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp,
+                                     _dp]
+    lib.oracle_lse_merge.restype = ctypes.c_int
     lib.oracle_set_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -102,6 +105,22 @@ def attention_fwd_rows(q_rows, qpos, k, v, scale, causal, return_p=False):
                                  _p(lse), _p(P) if return_p else None)
     _check(rc, "fwd_rows")
     return (o, lse, P) if return_p else (o, lse)
+
+
+def lse_merge(o_parts, lse_parts):
+    """Merge partial attention results over disjoint key sets, in fp64.
+
+    o_parts: [P, rows, d] normalised partial outputs; lse_parts: [P, rows]
+    their log-normalisers (-inf for a part with no visible key). Returns
+    (o [rows, d], lse [rows])."""
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    P, rows, d = o_parts.shape
+    assert lse_parts.shape == (P, rows)
+    o = np.empty((rows, d), dtype=np.float64)
+    lse = np.empty(rows, dtype=np.float64)
+    _check(_load().oracle_lse_merge(P, rows, d, _p(o_parts), _p(lse_parts), _p(o), _p(lse)),
+           "lse_merge")
+    return o, lse
 
 
 def attention_bwd(q, k, v, do, scale, causal, return_ds=False):

@@ -273,3 +273,50 @@ int oracle_bwd(int N, const double *Q, const double *K, const double *V,
   free(O);
   return ORACLE_OK;
 }
+
+/* Merge of partial results over disjoint key sets ("Flash Attention" notes,
+ * section 2, parts 3.1 and 4.1: the two-block merge of (m, l) and of the
+ * unnormalised output O~, which is associative, so blocks may be combined in
+ * any grouping).
+ *
+ * Part s holds, for each of `rows` rows, a normalised output O_s (d values)
+ * and its log-normaliser LSE_s. It enters the merge as the block
+ * (m = LSE_s, l = 1, O~ = O_s), for which m + log l = LSE_s and O~ / l = O_s.
+ * Parts are folded left to right:
+ *   m = max(m_A, m_B),  l = l_A e^(m_A - m) + l_B e^(m_B - m),
+ *   O~ = O~_A e^(m_A - m) + O~_B e^(m_B - m),
+ * and the result is O = O~ / l, LSE = m + log l. A part with LSE_s = -inf
+ * (no visible key) contributes nothing; a row whose parts are all -inf gets
+ * O = 0 and LSE = -inf.
+ * Layout: O_parts [parts][rows][d], LSE_parts [parts][rows]; O [rows][d],
+ * LSE [rows]. */
+int oracle_lse_merge(int parts, int rows, int d, const double *O_parts,
+                     const double *LSE_parts, double *O, double *LSE) {
+  if (parts <= 0 || rows <= 0 || d <= 0 || !O_parts || !LSE_parts || !O || !LSE)
+    return ORACLE_EINVAL;
+  int i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < rows; ++i) {
+    double m = -INFINITY, l = 0.0;
+    double *acc = O + (size_t)i * d;
+    for (int c = 0; c < d; ++c) acc[c] = 0.0;
+    for (int s = 0; s < parts; ++s) {
+      const double mb = LSE_parts[(size_t)s * rows + i];
+      if (mb == -INFINITY) continue;
+      const double *ob = O_parts + ((size_t)s * rows + i) * d;
+      const double mn = m > mb ? m : mb;
+      const double fa = (m == -INFINITY) ? 0.0 : exp(m - mn);
+      const double fb = exp(mb - mn);
+      l = l * fa + 1.0 * fb;
+      for (int c = 0; c < d; ++c) acc[c] = acc[c] * fa + ob[c] * fb;
+      m = mn;
+    }
+    if (l > 0.0) {
+      for (int c = 0; c < d; ++c) acc[c] /= l;
+      LSE[i] = m + log(l);
+    } else {
+      LSE[i] = -INFINITY;
+    }
+  }
+  return ORACLE_OK;
+}

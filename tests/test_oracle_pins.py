@@ -384,3 +384,69 @@ def test_thread_count_does_not_change_results(oracle_lib):
         oracle_lib.set_num_threads(n0)
     for key in ("dq", "dk", "dv", "D"):
         assert np.array_equal(a[key], b[key])
+
+
+# ---------------------------------------------------------------------------
+# The merge of partial results (Online Softmax parts 3.1 and 4.1), as used
+# by the split-KV forward: pinned against the forward's plain definition.
+# ---------------------------------------------------------------------------
+
+def _partials_over_key_sets(oracle_lib, q, k, v, scale, key_sets):
+    """Non-causal attention of every query over each key subset, by the
+    oracle's plain definition restricted to those keys."""
+    qpos = np.arange(q.shape[0])
+    o_parts, lse_parts = [], []
+    for ks in key_sets:
+        o, lse = oracle_lib.attention_fwd_rows(q, qpos, k[ks], v[ks], scale, False)
+        o_parts.append(o)
+        lse_parts.append(lse)
+    return np.stack(o_parts), np.stack(lse_parts)
+
+
+@pytest.mark.parametrize("split", ["contiguous", "strided", "uneven"])
+def test_lse_merge_of_key_subsets_equals_full_attention(oracle_lib, split):
+    """Attention over disjoint key subsets, merged, is attention over all
+    keys (the merge is exact, not an approximation)."""
+    rng = _rng(11)
+    N, d, scale = 41, 6, 0.4
+    q = rng.standard_normal((N, d)) * 2.0
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    keys = np.arange(N)
+    if split == "contiguous":
+        sets = [keys[:10], keys[10:30], keys[30:]]
+    elif split == "strided":
+        sets = [keys[r::4] for r in range(4)]
+    else:
+        sets = [keys[:1], keys[1:2], keys[2:]]
+    o_parts, lse_parts = _partials_over_key_sets(oracle_lib, q, k, v, scale, sets)
+    o, lse = oracle_lib.lse_merge(o_parts, lse_parts)
+    o_ref, lse_ref = oracle_lib.attention_fwd(q, k, v, scale, False)
+    assert np.allclose(o, o_ref, rtol=1e-13, atol=1e-13)
+    assert np.allclose(lse, lse_ref, rtol=1e-13, atol=1e-13)
+
+
+def test_lse_merge_ignores_empty_parts_and_order(oracle_lib):
+    """A part with LSE = -inf (no visible key) contributes nothing, the
+    order of the parts does not matter, a single part passes through, and a
+    row with only empty parts gets O = 0, LSE = -inf."""
+    rng = _rng(12)
+    N, d, scale = 17, 5, 0.6
+    q = rng.standard_normal((N, d)); k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    keys = np.arange(N)
+    o_parts, lse_parts = _partials_over_key_sets(oracle_lib, q, k, v, scale,
+                                                 [keys[:7], keys[7:]])
+    o2, lse2 = oracle_lib.lse_merge(o_parts, lse_parts)
+    junk = rng.standard_normal((1, N, d)) * 1e3
+    o3, lse3 = oracle_lib.lse_merge(np.concatenate([o_parts[:1], junk, o_parts[1:]]),
+                                    np.concatenate([lse_parts[:1], np.full((1, N), -np.inf),
+                                                    lse_parts[1:]]))
+    assert np.allclose(o3, o2, rtol=1e-14, atol=1e-14) and np.allclose(lse3, lse2, rtol=1e-14)
+    o4, lse4 = oracle_lib.lse_merge(o_parts[::-1], lse_parts[::-1])
+    assert np.allclose(o4, o2, rtol=1e-13, atol=1e-13) and np.allclose(lse4, lse2, rtol=1e-13)
+    o1, lse1 = oracle_lib.lse_merge(o_parts[:1], lse_parts[:1])
+    assert np.allclose(o1, o_parts[0], rtol=1e-14, atol=1e-14)
+    assert np.array_equal(lse1, lse_parts[0])
+    o0, lse0 = oracle_lib.lse_merge(junk, np.full((1, N), -np.inf))
+    assert np.all(o0 == 0.0) and np.all(lse0 == -np.inf)
