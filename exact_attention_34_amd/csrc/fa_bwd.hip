@@ -23,6 +23,7 @@
 // products per tile pair); on this chip that is cheaper than summing dQ
 // through fp32 atomics in L2, and every gradient is deterministic.
 
+#include <limits.h>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -147,29 +148,24 @@ struct DkdvCfg {
 // the second half its dS arithmetic runs beside role 0's dV MFMAs. Query
 // tiles (Q, dO, LSE, D) are triple-buffered (the tile being read, the
 // previous one for role 1's dK, and the next one being loaded).
+//
+// One key block (block kb of slice bh). Query-tile buffers: buffer b holds Q
+// at qo + 2*b*QTILE, dO right after it, and LSE, D rows at lv + 2*b*BR; px
+// is the P hand-over area, PX floats per key slice.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
+__device__ __forceinline__ void dkdv_block(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dK,
-    uint16_t *__restrict__ dV, int N, int nkb, int total, float c2, float scale) {
+    uint16_t *__restrict__ dV, int N, int bh, int kb, float c2, float scale, uint16_t *qo,
+    float *lv, float *px) {
   using C = DkdvCfg<D>;
   constexpr int NT = C::NT;
-  // Query-tile buffers: buffer b holds Q at qo + 2*b*QTILE, dO right after
-  // it, and LSE, D rows at lv + 2*b*BR; then the P hand-over area, PX floats
-  // per key slice.
-  __shared__ __attribute__((aligned(1024))) uint16_t qo[2 * C::NBUF * C::QTILE];
-  __shared__ __attribute__((aligned(256))) float lv[2 * C::NBUF * C::BR];
-  __shared__ __attribute__((aligned(1024))) float px[4 * C::PX];
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int l32 = lane & 31, g = lane >> 5;
   const int ks = w & 3;     // key slice: keys 32 ks .. +31 of the block
   const int role = w >> 2;  // 0: S, P, dV; 1: dP, dS, dK
-  const int tile = xcd_tile(blockIdx.x, total);
-  const int bh = tile / nkb;
-  const int kb = tile - bh * nkb;
   const int k0 = kb * C::KB;
   const int wk0 = k0 + 32 * ks;  // first key of this wave
   const int mykey = wk0 + l32;   // key of this lane's S/P column
@@ -316,12 +312,15 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
       rows_x_kv(s, Qs);  // S = Q K^T
       pipeline(KR{}, I1{}, I6{});
       if (need_mask) {
+        // Query q0 + 4g + off sees this lane's key iff lo <= off <= hi.
+        const int hi = (mykey < N ? N - 1 : -1) - q0 - 4 * g;
+        const int lo = CAUSAL ? mykey - q0 - 4 * g : INT_MIN;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int q = q0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (q >= N || mykey >= N || (CAUSAL && mykey > q)) s[t][r] = -INFINITY;
+            const int off = 32 * t + 8 * (r >> 2) + (r & 3);
+            if (off > hi || (CAUSAL && off < lo)) s[t][r] = -INFINITY;
           }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -398,6 +397,31 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
   }
 }
 
+// Work units: without the causal mask, one key block. With it, key block kb
+// sweeps the query tiles from its own first row on, so blocks are paired as
+// (p, nkb - 1 - p), which gives every unit the same number of query tiles
+// (as in the forward).
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
+    const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dK,
+    uint16_t *__restrict__ dV, int N, int nkb, int nunits, int total, float c2, float scale) {
+  using C = DkdvCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t qo[2 * C::NBUF * C::QTILE];
+  __shared__ __attribute__((aligned(256))) float lv[2 * C::NBUF * C::BR];
+  __shared__ __attribute__((aligned(1024))) float px[4 * C::PX];
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int bh = tile / nunits;
+  const int u = tile - bh * nunits;
+  dkdv_block<T, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dK, dV, N, bh, u, c2, scale, qo, lv, px);
+  if (CAUSAL && u != nkb - 1 - u) {
+    __syncthreads();  // every wave is done with the LDS tiles
+    dkdv_block<T, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dK, dV, N, bh, nkb - 1 - u, c2, scale, qo,
+                             lv, px);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dQ: query blocks outer, key tiles inner.
 // ---------------------------------------------------------------------------
@@ -419,23 +443,19 @@ struct DqCfg {
 // and 16 keys per lane in the B-operand layout of dQ^T += K^T dS^T, whose K^T
 // operand comes from the same K tile with transposing reads. K and V tiles
 // are double-buffered in LDS and filled by direct buffer -> LDS loads.
+//
+// One block of query rows (block qb of slice bh). LDS buffer b: K tile at
+// kv + 2*b*TILE, V tile right after it.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+__device__ __forceinline__ void dq_block(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dQ,
-    int N, int nqb, int total, float c2, float scale) {
+    int N, int bh, int qb, float c2, float scale, uint16_t *kv) {
   using C = DqCfg<D>;
-  // Buffer b: K tile at kv + 2*b*TILE, V tile right after it.
-  __shared__ __attribute__((aligned(1024))) uint16_t kv[4 * C::TILE];
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int tile = xcd_tile(blockIdx.x, total);
-  const int bh = tile / nqb;
-  int qb = tile - bh * nqb;
-  if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
   const int q0 = qb * C::BR;
   const int wq0 = q0 + 32 * w;  // first query row of this wave
   const int qrow = wq0 + l32;
@@ -518,11 +538,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (need_mask) {
+      // Key kb + 32t + 4g + off is visible iff off <= lim.
+      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kb - 32 * t - 4 * g;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (key >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
     }
     __builtin_amdgcn_sched_barrier(0);
     // P = 2^(S*scale*log2e - LSE*log2e), dS = P o (dP - D), rounded to T in
@@ -606,6 +626,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   }
 }
 
+// Work units as in the forward: one query block, or under the causal mask
+// the pair (nqb - 1 - p, p) of blocks with equal total length.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
+    const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dQ,
+    int N, int nqb, int nunits, int total, float c2, float scale) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t kv[4 * C::TILE];
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int bh = tile / nunits;
+  const int u = tile - bh * nunits;
+  if (!CAUSAL) {
+    dq_block<T, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
+    return;
+  }
+  dq_block<T, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, nqb - 1 - u, c2, scale, kv);
+  if (u != nqb - 1 - u) {
+    __syncthreads();  // every wave is done with the LDS tiles
+    dq_block<T, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -638,10 +682,11 @@ template <typename T, int D, bool CAUSAL>
 static hipError_t dkdv(const BwdArgs &a, void *dK, void *dV, hipStream_t st) {
   using C = DkdvCfg<D>;
   const int nkb = (a.N + C::KB - 1) / C::KB;
-  const int total = nkb * a.BH;
+  const int nunits = CAUSAL ? (nkb + 1) / 2 : nkb;
+  const int total = nunits * a.BH;
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
                      a.Q, a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N, nkb,
-                     total, a.c2, a.scale);
+                     nunits, total, a.c2, a.scale);
   return hipGetLastError();
 }
 
@@ -649,10 +694,11 @@ template <typename T, int D, bool CAUSAL>
 static hipError_t dq(const BwdArgs &a, void *dQ, hipStream_t st) {
   using C = DqCfg<D>;
   const int nqb = (a.N + C::BR - 1) / C::BR;
-  const int total = nqb * a.BH;
+  const int nunits = CAUSAL ? (nqb + 1) / 2 : nqb;
+  const int total = nunits * a.BH;
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st, a.Q,
-                     a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dQ, a.N, nqb, total, a.c2,
-                     a.scale);
+                     a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dQ, a.N, nqb, nunits, total,
+                     a.c2, a.scale);
   return hipGetLastError();
 }
 

@@ -76,24 +76,19 @@ __device__ __forceinline__ int swz_v(int row) {
 // runs on the vector ALUs, the matrix cores already compute the scores of
 // tile j + 1, so that each wave keeps both busy. K tiles are therefore
 // loaded two tiles ahead and V tiles one tile ahead.
+//
+// One block of BR query rows (block qb of slice bh); K0, K1, V0, V1 are the
+// workgroup's LDS tiles.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void fwd_b16_kernel(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int N,
-    int nqb, int total, float c2) {
+__device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
+                                          const uint16_t *__restrict__ K,
+                                          const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
+                                          float *__restrict__ LSE, int N, int bh, int qb, float c2,
+                                          uint16_t *K0, uint16_t *K1, uint16_t *V0, uint16_t *V1) {
   using C = FwdCfg<D>;
-  // Two buffers per tensor, named separately so that the compiler can tell
-  // the direct loads into one from the reads of the other.
-  __shared__ __attribute__((aligned(1024))) uint16_t K0[C::TILE], K1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t V0[C::TILE], V1[C::TILE];
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int l32 = lane & 31, g = lane >> 5;
-  const int tile = xcd_tile(blockIdx.x, total);
-  const int bh = tile / nqb;
-  int qb = tile - bh * nqb;
-  if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
   const int q0 = qb * C::BR;
   const int wq0 = q0 + 32 * w;  // first query row of this wave
   const int qrow = wq0 + l32;
@@ -230,13 +225,13 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void
     s_mfma(sn, Kn, 0);
     __builtin_amdgcn_sched_barrier(0);
     if ((kb + C::BC > N) || (CAUSAL && kb + C::BC - 1 > wq0)) {
+      // Key kb + 4g + off is visible iff off <= lim (one compare per score).
+      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kb - 4 * g;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= N || (CAUSAL && key > qrow)) s[t][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * t + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = -INFINITY;
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -346,6 +341,36 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void
         *(u32x2 *)(Orow + 32 * dt + 8 * i + 4 * g) = v;
       }
     if (g == 0) LSE[(size_t)bh * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+// Work units: without the causal mask, one query block. With it, block qb
+// sweeps 2(qb + 1) key tiles, so blocks are paired as (nqb - 1 - p, p): every
+// unit then sweeps the same number of tiles (nqb + 1 pairs), which keeps the
+// two workgroup slots of each CU refilled at an even pace (with units of
+// unequal length, freed slots were observed to stay empty for several
+// microseconds), and halves the number of workgroup start-ups.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void fwd_b16_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int N,
+    int nqb, int nunits, int total, float c2) {
+  using C = FwdCfg<D>;
+  // Two buffers per tensor, named separately so that the compiler can tell
+  // the direct loads into one from the reads of the other.
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[C::TILE], K1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[C::TILE], V1[C::TILE];
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int bh = tile / nunits;
+  const int u = tile - bh * nunits;
+  if (!CAUSAL) {
+    fwd_block<T, D, CAUSAL>(Q, K, V, O, LSE, N, bh, u, c2, K0, K1, V0, V1);
+    return;
+  }
+  fwd_block<T, D, CAUSAL>(Q, K, V, O, LSE, N, bh, nqb - 1 - u, c2, K0, K1, V0, V1);
+  if (u != nqb - 1 - u) {
+    __syncthreads();  // every wave is done with the LDS tiles
+    fwd_block<T, D, CAUSAL>(Q, K, V, O, LSE, N, bh, u, c2, K0, K1, V0, V1);
   }
 }
 
@@ -482,10 +507,11 @@ static hipError_t fwd_b16(int BH, int N, const void *Q, const void *K, const voi
                           void *O, float *LSE, hipStream_t st) {
   using C = FwdCfg<D>;
   const int nqb = (N + C::BR - 1) / C::BR;
-  const int total = nqb * BH;
+  const int nunits = CAUSAL ? (nqb + 1) / 2 : nqb;
+  const int total = nunits * BH;
   hipLaunchKernelGGL((fwd_b16_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
                      (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                     (uint16_t *)O, LSE, N, nqb, total, c2);
+                     (uint16_t *)O, LSE, N, nqb, nunits, total, c2);
   return hipGetLastError();
 }
 
