@@ -23,6 +23,9 @@ Prints ONE JSON line. Besides the required keys it carries:
                 workload (also used as a parity spot-check of the timed run);
   sweep         forward and forward+backward TFLOPS for bf16 d = 128 at
                 N = 2048, 4096, 8192 (B*N = 16384 tokens, 16 heads).
+  splitkv       fa_fwd against fa_fwd_splitkv (the library's split choice) on
+                grids with fewer query blocks than the chip has workgroup
+                slots, and the merge kernel's HBM rate.
 """
 import argparse
 import hashlib
@@ -199,6 +202,74 @@ def cpu_baseline(w, host, outs, min_seconds=10.0, max_slices=256):
                       "(%.1f s)" % (n, w.B * w.H, t_total)}, worst
 
 
+def _time_ms(torch, fn, iters, settle_s):
+    t_start = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    while time.perf_counter() - t_start < settle_s:
+        fn()
+        torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def splitkv_report(fa, torch, settle_s):
+    """Forward with and without key splits where the plain grid under-fills
+    the chip; the merge kernel timed alone on the same partial results."""
+    import attn_inputs as ai
+    L = fa.lib()
+    out = []
+    cases = [ai.WORKLOADS["c2"],
+             ai.custom("b1-h4-n8192", 1, 4, 8192, 128, "bf16", False, seed=42),
+             ai.custom("b1-h4-n8192-causal", 1, 4, 8192, 128, "bf16", True, seed=42)]
+    for w in cases:
+        d = {k: v.cuda() for k, v in ai.make_inputs(w, with_do=False).items()}
+        B, H, N, D = w.B, w.H, w.N, w.d
+        code = {torch.bfloat16: fa.BF16, torch.float16: fa.F16}[d["q"].dtype]
+        parts = fa.fwd_splitkv_parts(B, H, N, 0)
+        nbytes = fa.fwd_splitkv_workspace_bytes(d["q"].dtype, B, H, N, D, 0)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(d["q"])
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        st = torch.cuda.current_stream().cuda_stream
+        P = lambda t: t.data_ptr()
+
+        def plain():
+            L.fa_fwd(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), w.scale,
+                     int(w.causal), P(o), P(lse), st)
+
+        def split():
+            L.fa_fwd_splitkv(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), w.scale,
+                             int(w.causal), 0, P(o), P(lse), P(ws), nbytes, st)
+
+        rows = B * H * N
+        obytes = -(-parts * rows * D * 4 // 256) * 256
+
+        def merge():
+            L.fa_lse_merge(code, parts, rows, D, P(ws), P(ws) + obytes, P(o), P(lse), st)
+
+        ms_plain = _time_ms(torch, plain, 20, settle_s)
+        ms_split = _time_ms(torch, split, 20, settle_s)
+        ms_merge = _time_ms(torch, merge, 20, 0.0)
+        merge_bytes = parts * rows * (4 * D + 4) + rows * (2 * D + 4)
+        out.append({"workload": w.name, "B": B, "H": H, "N": N, "d": D, "causal": w.causal,
+                    "parts": parts, "fwd_tflops": round(w.fwd_flops() / ms_plain / 1e9, 1),
+                    "splitkv_tflops": round(w.fwd_flops() / ms_split / 1e9, 1),
+                    "ms_fwd": round(ms_plain, 4), "ms_splitkv": round(ms_split, 4),
+                    "merge_ms": round(ms_merge, 4),
+                    "merge_gbs": round(merge_bytes / ms_merge / 1e6, 1)})
+        print("# splitkv %s parts %d: fwd %.3f ms, split %.3f ms (merge %.3f ms, %.0f GB/s)" %
+              (w.name, parts, ms_plain, ms_split, ms_merge, merge_bytes / ms_merge / 1e6),
+              file=sys.stderr, flush=True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +280,7 @@ def main():
     ap.add_argument("--workload", default="c5")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-splitkv", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales the HBM "
                          "byte counters read under rocprofv3)")
@@ -292,6 +364,8 @@ def main():
             print("# sweep %s fwd %.1f TFLOPS fwd+bwd %.1f TFLOPS" % (name, ff, tf),
                   file=sys.stderr, flush=True)
         out["sweep"] = sweep
+    if not args.no_splitkv:
+        out["splitkv"] = splitkv_report(fa, torch, min(args.settle, 0.5))
     print(json.dumps(out), flush=True)
 
 

@@ -13,7 +13,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq",
+__all__ = ["fwd", "fwd_splitkv", "fwd_splitkv_parts", "fwd_splitkv_workspace_bytes",
+           "lse_merge", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq",
            "bwd_workspace_bytes", "FAError", "library_path", "lib",
            "F32", "F16", "BF16"]
 
@@ -51,6 +52,14 @@ def lib():
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_fwd.argtypes = [i, i, i, i, i, p, p, p, f, i, p, p, p]
     L.fa_fwd.restype = i
+    L.fa_fwd_splitkv.argtypes = [i, i, i, i, i, p, p, p, f, i, i, p, p, p, z, p]
+    L.fa_fwd_splitkv.restype = i
+    L.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.fa_fwd_splitkv_workspace_bytes.restype = z
+    L.fa_fwd_splitkv_parts.argtypes = [i, i, i, i]
+    L.fa_fwd_splitkv_parts.restype = i
+    L.fa_lse_merge.argtypes = [i, i, ctypes.c_longlong, i, p, p, p, p, p]
+    L.fa_lse_merge.restype = i
     L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     L.fa_bwd_workspace_bytes.restype = z
     L.fa_bwd.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, p, p, z, p]
@@ -106,6 +115,48 @@ def fwd(q, k, v, scale=None, causal=False):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _call("fa_fwd", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _scale(scale, d),
           int(bool(causal)), _ptr(o), _ptr(lse), _stream(q))
+    return o, lse
+
+
+def fwd_splitkv_workspace_bytes(dtype, B, H, N, d, nsplit=0):
+    return int(lib().fa_fwd_splitkv_workspace_bytes(_CODES[dtype], B, H, N, d, int(nsplit)))
+
+
+def fwd_splitkv_parts(B, H, N, nsplit=0):
+    """Key ranges fwd_splitkv uses for this nsplit (0: the library's choice)."""
+    return int(lib().fa_fwd_splitkv_parts(B, H, N, int(nsplit)))
+
+
+def fwd_splitkv(q, k, v, scale=None, causal=False, nsplit=0, workspace=None):
+    """O, LSE as fwd(), with each row's keys split into ranges swept by separate
+    workgroups and the partial results merged (nsplit=0: the library picks)."""
+    dt, B, H, N, d = _check_qkv(q, k, v)
+    nbytes = fwd_splitkv_workspace_bytes(q.dtype, B, H, N, d, nsplit)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _call("fa_fwd_splitkv", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _scale(scale, d),
+          int(bool(causal)), int(nsplit), _ptr(o), _ptr(lse), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(q))
+    return o, lse
+
+
+def lse_merge(o_parts, lse_parts, out_dtype=torch.float32):
+    """Merge partial results over disjoint key sets.
+
+    o_parts: fp32 [P, rows, d]; lse_parts: fp32 [P, rows] (-inf: empty part).
+    Returns (o [rows, d] in out_dtype, lse fp32 [rows])."""
+    if o_parts.dim() != 3 or lse_parts.shape != o_parts.shape[:2]:
+        raise ValueError("expected o_parts [P, rows, d] and lse_parts [P, rows]")
+    for t in (o_parts, lse_parts):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("parts must be contiguous fp32 GPU tensors")
+    P, rows, d = o_parts.shape
+    o = torch.empty((rows, d), dtype=out_dtype, device=o_parts.device)
+    lse = torch.empty(rows, dtype=torch.float32, device=o_parts.device)
+    _call("fa_lse_merge", _CODES[out_dtype], P, rows, d, _ptr(o_parts), _ptr(lse_parts),
+          _ptr(o), _ptr(lse), _stream(o_parts))
     return o, lse
 
 

@@ -41,6 +41,42 @@ int status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
 size_t d_bytes(int B, int H, int N) { return round_up((size_t)B * H * N * sizeof(float), kWsAlign); }
 
+constexpr int kMaxSplit = 64;
+
+// Key ranges for fa_fwd_splitkv when the caller passes 0: enough workgroups
+// (one per slice, range and 128-row query block) to give every compute unit
+// two, with at least 16 key tiles per range (shorter ranges do not repay the
+// extra kernel and the merge: at B2 H8 N1024 two ranges of 8 tiles ran
+// 0.017 ms and four of 4 tiles 0.022 ms, against 0.015 ms unsplit).
+int auto_split(int B, int H, int N) {
+  int cus = 256, dev = 0, v = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+    cus = v;
+  const long units = (long)B * H * ((N + 127) / 128);
+  long ns = (2L * cus + units - 1) / units;
+  const long tiles = (N + 63) / 64;
+  if (ns > tiles / 16) ns = tiles / 16;
+  if (ns > kMaxSplit) ns = kMaxSplit;
+  return ns < 1 ? 1 : (int)ns;
+}
+
+// Requested split count -> ranges actually used (0 if invalid).
+int resolve_split(int B, int H, int N, int nsplit) {
+  if (nsplit < 0 || nsplit > kMaxSplit) return 0;
+  if (nsplit == 0) nsplit = auto_split(B, H, N);
+  return fa::split_parts(N, nsplit);
+}
+
+// Workspace of the split forward for `parts` ranges: O parts, then LSE parts.
+size_t split_o_bytes(int parts, int B, int H, int N, int d) {
+  return round_up((size_t)parts * B * H * N * d * sizeof(float), kWsAlign);
+}
+size_t split_bytes(int parts, int B, int H, int N, int d) {
+  return split_o_bytes(parts, B, H, N, d) +
+         round_up((size_t)parts * B * H * N * sizeof(float), kWsAlign);
+}
+
 }  // namespace
 
 extern "C" {
@@ -67,6 +103,55 @@ int fa_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, 
     return FA_ERR_INVALID_ARG;
   return status(fa::launch_fwd(dtype, B, H, N, d, Q, K, V, scale, causal, O, LSE,
                                (hipStream_t)stream));
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int dtype, int B, int H, int N, int d, int nsplit) {
+  if (check_shape(dtype, B, H, N, d, false) != FA_OK || dtype == FA_F32) return 0;
+  const int parts = resolve_split(B, H, N, nsplit);
+  if (parts == 0) return 0;
+  return split_bytes(parts, B, H, N, d);
+}
+
+int fa_fwd_splitkv_parts(int B, int H, int N, int nsplit) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return resolve_split(B, H, N, nsplit);
+}
+
+int fa_lse_merge(int dtype, int parts, long long rows, int d, const float *O_parts,
+                 const float *LSE_parts, void *O, float *LSE, void *stream) {
+  if (parts <= 0 || rows <= 0) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)parts * rows * d >= (1LL << 40) || rows * (d / 4) >= (1LL << 31) * 256LL)
+    return FA_ERR_INVALID_ARG;
+  if (!tensor_ok(O_parts) || !vec_ok(LSE_parts) || !tensor_ok(O) || !vec_ok(LSE))
+    return FA_ERR_INVALID_ARG;
+  return status(fa::launch_lse_merge(dtype, parts, (long)rows, d, O_parts, LSE_parts, O, LSE,
+                                     (hipStream_t)stream));
+}
+
+int fa_fwd_splitkv(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                   const void *V, float scale, int causal, int nsplit, void *O, float *LSE,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shape(dtype, B, H, N, d, false);
+  if (rc != FA_OK) return rc;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((rc = check_scale_causal(scale, causal)) != FA_OK) return rc;
+  if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O) || !vec_ok(LSE) ||
+      !tensor_ok(workspace))
+    return FA_ERR_INVALID_ARG;
+  if (nsplit < 0 || nsplit > kMaxSplit) return FA_ERR_INVALID_ARG;
+  const int req = nsplit == 0 ? auto_split(B, H, N) : nsplit;
+  const int parts = fa::split_parts(N, req);
+  if (workspace_bytes < split_bytes(parts, B, H, N, d)) return FA_ERR_WORKSPACE;
+  float *Op = (float *)workspace;
+  float *Lp = (float *)((char *)workspace + split_o_bytes(parts, B, H, N, d));
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = status(fa::launch_fwd_split(dtype, B, H, N, d, Q, K, V, scale, causal, req, Op, Lp,
+                                        st))) != FA_OK)
+    return rc;
+  return status(
+      fa::launch_lse_merge(dtype, parts, (long)B * H * N, d, Op, Lp, O, LSE, st));
 }
 
 size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d) {

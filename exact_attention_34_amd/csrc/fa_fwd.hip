@@ -77,14 +77,20 @@ __device__ __forceinline__ int swz_v(int row) {
 // tile j + 1, so that each wave keeps both busy. K tiles are therefore
 // loaded two tiles ahead and V tiles one tile ahead.
 //
-// One block of BR query rows (block qb of slice bh); K0, K1, V0, V1 are the
-// workgroup's LDS tiles.
-template <typename T, int D, bool CAUSAL>
+// One block of BR query rows (block qb of slice bh) against the keys in
+// [kfirst, klim) (kfirst a multiple of BC; the whole row is [0, N)); K0, K1,
+// V0, V1 are the workgroup's LDS tiles. PART = false writes O (in T,
+// normalised) and LSE; PART = true writes the partial result of this key
+// range in fp32 to Op / Lp: O~ / l and m + log l, or 0 and -inf for a row
+// that sees none of these keys.
+template <typename T, int D, bool CAUSAL, bool PART>
 __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
                                           const uint16_t *__restrict__ K,
                                           const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
-                                          float *__restrict__ LSE, int N, int bh, int qb, float c2,
-                                          uint16_t *K0, uint16_t *K1, uint16_t *V0, uint16_t *V1) {
+                                          float *__restrict__ LSE, float *__restrict__ Op,
+                                          float *__restrict__ Lp, int N, int bh, int qb,
+                                          int kfirst, int klim, float c2, uint16_t *K0,
+                                          uint16_t *K1, uint16_t *V0, uint16_t *V1) {
   using C = FwdCfg<D>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -102,8 +108,8 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
 #pragma unroll
   for (int c = 0; c < C::NCH; ++c) qreg[c] = ld128(Qh + (size_t)qld * D + 16 * c + 8 * g);
 
-  const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
-  const int ntiles = (kend + C::BC - 1) / C::BC;
+  const int kend = CAUSAL ? min(klim, q0 + C::BR) : klim;
+  const int ntiles = max(kend - kfirst + C::BC - 1, 0) / C::BC;
 
   // Direct buffer -> LDS loads: instruction i of wave w fills LDS chunks
   // (w*LPW + i)*64 + lane; this lane fetches the global chunk that belongs
@@ -120,9 +126,9 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
   // range check makes the loads of rows past them -- or of a whole tile past
   // the last one -- write zeros, whose keys are masked.
   auto tile_rsrc = [&](const uint16_t *src, int kt) __attribute__((always_inline)) {
-    const int kb = kt * C::BC;
+    const int kb = kfirst + kt * C::BC;
     const int rows = max(min(kend - kb, C::BC), 0);
-    return make_rsrc(src + (size_t)kb * D, (uint32_t)rows * D * 2);
+    return make_rsrc(src + (size_t)min(kb, N) * D, (uint32_t)rows * D * 2);
   };
   // Load i of this wave for tile kt of one tensor into the LDS tile dst.
   auto dma = [&](const i32x4 &rs, const int (&go)[C::LPW], uint16_t *dst, int i)
@@ -210,7 +216,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
   // tile kt + 1 (from K buffer b ^ 1; past the last tile the result is
   // unused). V of tile kt is in V buffer b.
   auto step = [&](int kt, f32x16 (&s)[NT], f32x16 (&sn)[NT], int b) __attribute__((always_inline)) {
-    const int kb = kt * C::BC;
+    const int kb = kfirst + kt * C::BC;
     // Every wave's loads of K (kt + 1) and V (kt) have landed, and every wave
     // is done with K buffer b (read for tile kt) and V buffer b ^ 1, which
     // receive K (kt + 2) in phase A and V (kt + 1) in phase B.
@@ -224,9 +230,9 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
     __builtin_amdgcn_sched_barrier(0);
     s_mfma(sn, Kn, 0);
     __builtin_amdgcn_sched_barrier(0);
-    if ((kb + C::BC > N) || (CAUSAL && kb + C::BC - 1 > wq0)) {
+    if ((kb + C::BC > klim) || (CAUSAL && kb + C::BC - 1 > wq0)) {
       // Key kb + 4g + off is visible iff off <= lim (one compare per score).
-      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kb - 4 * g;
+      const int lim = (CAUSAL ? min(qrow, klim - 1) : klim - 1) - kb - 4 * g;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -329,6 +335,24 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
   // Epilogue: O = O~ / l, LSE = (m + log2 l) * ln 2.
   const float l_tot = pair_sum(l_run);
   const float inv = fast_rcp(l_tot);
+  if (PART) {
+    if (qrow < N) {
+      const bool any = l_tot > 0.f;
+      const float f = any ? inv : 0.f;
+      float *Orow = Op + base + (size_t)qrow * D;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 v = {o[dt][4 * i] * f, o[dt][4 * i + 1] * f, o[dt][4 * i + 2] * f,
+                           o[dt][4 * i + 3] * f};
+          *(f32x4 *)(Orow + 32 * dt + 8 * i + 4 * g) = v;
+        }
+      if (g == 0)
+        Lp[(size_t)bh * N + qrow] = any ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   if (qrow < N) {
     uint16_t *Orow = O + base + (size_t)qrow * D;
 #pragma unroll
@@ -364,15 +388,97 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void
   const int bh = tile / nunits;
   const int u = tile - bh * nunits;
   if (!CAUSAL) {
-    fwd_block<T, D, CAUSAL>(Q, K, V, O, LSE, N, bh, u, c2, K0, K1, V0, V1);
+    fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, bh, u, 0, N, c2, K0, K1,
+                                   V0, V1);
     return;
   }
-  fwd_block<T, D, CAUSAL>(Q, K, V, O, LSE, N, bh, nqb - 1 - u, c2, K0, K1, V0, V1);
+  fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, bh, nqb - 1 - u, 0, N, c2,
+                                 K0, K1, V0, V1);
   if (u != nqb - 1 - u) {
     __syncthreads();  // every wave is done with the LDS tiles
-    fwd_block<T, D, CAUSAL>(Q, K, V, O, LSE, N, bh, u, c2, K0, K1, V0, V1);
+    fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, bh, u, 0, N, c2, K0, K1,
+                                   V0, V1);
   }
 }
+
+// Split-key forward: the keys of every row are cut into nsplit ranges of
+// split_keys keys (a multiple of the tile width), and each (slice, range,
+// query block) is one workgroup, which writes its partial result in fp32:
+// part s of slice bh at Op + (s * BH + bh) * N * D and Lp + (s * BH + bh) * N.
+// Workgroups of one slice and range are consecutive, so they share their K
+// and V tiles in one L2. The partials are combined by lse_merge_kernel.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void fwd_split_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, float *__restrict__ Op, float *__restrict__ Lp, int N,
+    int BH, int nqb, int nsplit, int split_keys, int total, float c2) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[C::TILE], K1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[C::TILE], V1[C::TILE];
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int per_bh = nsplit * nqb;
+  const int bh = tile / per_bh;
+  const int r = tile - bh * per_bh;
+  const int sp = r / nqb, qb = r - sp * nqb;
+  const int kfirst = sp * split_keys;
+  const int klim = min(N, kfirst + split_keys);
+  const size_t part = (size_t)sp * BH;
+  fwd_block<T, D, CAUSAL, true>(Q, K, V, nullptr, nullptr, Op + part * N * D, Lp + part * N, N,
+                                bh, qb, kfirst, klim, c2, K0, K1, V0, V1);
+}
+
+// Merge of partial results over disjoint key sets, per row r and part s:
+//   LSE_r = log sum_s exp(LSE_sr),  O_r = sum_s exp(LSE_sr - LSE_r) O_sr,
+// the closed form of folding the two-block merge of (m, l, O~) ("Flash
+// Attention" notes, section 2, parts 3.1 and 4.1) over the parts, with each
+// part entering as (LSE_s, 1, O_s). Parts with LSE = -inf are empty; a row
+// with only empty parts gets O = 0 and LSE = -inf. Each thread combines four
+// columns of one row (HBM-bound: parts * (4 d + 4) bytes read per row).
+template <typename TO>
+__global__ __launch_bounds__(256) void lse_merge_kernel(const float *__restrict__ Op,
+                                                         const float *__restrict__ Lp, int parts,
+                                                         long rows, int d,
+                                                         TO *__restrict__ O,
+                                                         float *__restrict__ LSE) {
+  const int tpr = d / 4;  // threads per row
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long row = t / tpr;
+  if (row >= rows) return;
+  const int c = 4 * (int)(t - row * tpr);
+  float m = -INFINITY;
+  for (int s = 0; s < parts; ++s) m = fmaxf(m, Lp[(size_t)s * rows + row]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < parts; ++s) {
+      const float ls = Lp[(size_t)s * rows + row];
+      if (ls == -INFINITY) continue;
+      const float wgt = fast_exp2((ls - m) * kLog2e);
+      const f32x4 v = *(const f32x4 *)(Op + ((size_t)s * rows + row) * d + c);
+      l += wgt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += wgt * v[e];
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if constexpr (std::is_same<TO, float>::value) {
+    const f32x4 v = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *(f32x4 *)(O + (size_t)row * d + c) = v;
+  } else {
+    u32x2 v;
+    v[0] = pack2<typename TO::Tag>(acc[0] * inv, acc[1] * inv);
+    v[1] = pack2<typename TO::Tag>(acc[2] * inv, acc[3] * inv);
+    *(u32x2 *)((uint16_t *)O + (size_t)row * d + c) = v;
+  }
+  if (c == 0) LSE[row] = l > 0.f ? m + logf(l) : -INFINITY;
+}
+
+// 16-bit output element of the merge (storage uint16_t, rounding by Tag).
+template <typename T>
+struct Out16 {
+  typedef T Tag;
+  uint16_t bits;
+};
 
 // fp32 inputs: the same sweep on v_mfma_f32_32x32x2_f32 (A: one value per
 // lane, row l % 32, k = l / 32), 32-key tiles, single-buffered LDS.
@@ -532,6 +638,57 @@ static hipError_t fwd_b16_c(int causal, int BH, int N, const void *Q, const void
                             const void *V, float c2, void *O, float *LSE, hipStream_t st) {
   return causal ? fwd_b16<T, D, true>(BH, N, Q, K, V, c2, O, LSE, st)
                 : fwd_b16<T, D, false>(BH, N, Q, K, V, c2, O, LSE, st);
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t fwd_split(int BH, int N, const void *Q, const void *K, const void *V, float c2,
+                            float *Op, float *Lp, int nsplit, int split_keys, hipStream_t st) {
+  using C = FwdCfg<D>;
+  const int nqb = (N + C::BR - 1) / C::BR;
+  const int total = BH * nsplit * nqb;
+  hipLaunchKernelGGL((fwd_split_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
+                     (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, Op, Lp, N, BH,
+                     nqb, nsplit, split_keys, total, c2);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t fwd_split_c(int causal, int BH, int N, const void *Q, const void *K,
+                              const void *V, float c2, float *Op, float *Lp, int nsplit,
+                              int split_keys, hipStream_t st) {
+  return causal ? fwd_split<T, D, true>(BH, N, Q, K, V, c2, Op, Lp, nsplit, split_keys, st)
+                : fwd_split<T, D, false>(BH, N, Q, K, V, c2, Op, Lp, nsplit, split_keys, st);
+}
+
+hipError_t launch_fwd_split(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                            const void *V, float scale, int causal, int nsplit, float *Op,
+                            float *Lp, hipStream_t st) {
+  const int BH = B * H;
+  const float c2 = scale * kLog2e;
+  const int split_keys = split_key_count(N, nsplit);
+  const int parts = split_parts(N, nsplit);
+  if (dtype == kBF16)
+    return d == 64 ? fwd_split_c<BF16, 64>(causal, BH, N, Q, K, V, c2, Op, Lp, parts, split_keys, st)
+                   : fwd_split_c<BF16, 128>(causal, BH, N, Q, K, V, c2, Op, Lp, parts, split_keys,
+                                            st);
+  return d == 64 ? fwd_split_c<F16, 64>(causal, BH, N, Q, K, V, c2, Op, Lp, parts, split_keys, st)
+                 : fwd_split_c<F16, 128>(causal, BH, N, Q, K, V, c2, Op, Lp, parts, split_keys, st);
+}
+
+hipError_t launch_lse_merge(int dtype, int parts, long rows, int d, const float *Op,
+                            const float *Lp, void *O, float *LSE, hipStream_t st) {
+  const long threads = rows * (d / 4);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (dtype == kF32)
+    hipLaunchKernelGGL((lse_merge_kernel<float>), dim3(blocks), dim3(256), 0, st, Op, Lp, parts,
+                       rows, d, (float *)O, LSE);
+  else if (dtype == kBF16)
+    hipLaunchKernelGGL((lse_merge_kernel<Out16<BF16>>), dim3(blocks), dim3(256), 0, st, Op, Lp,
+                       parts, rows, d, (Out16<BF16> *)O, LSE);
+  else
+    hipLaunchKernelGGL((lse_merge_kernel<Out16<F16>>), dim3(blocks), dim3(256), 0, st, Op, Lp,
+                       parts, rows, d, (Out16<F16> *)O, LSE);
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,

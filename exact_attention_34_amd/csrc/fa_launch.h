@@ -12,6 +12,28 @@ hipError_t launch_fwd(int dtype, int B, int H, int N, int d, const void *Q, cons
                       const void *V, float scale, int causal, void *O, float *LSE,
                       hipStream_t stream);
 
+// Split-key forward: key tiles (64 keys) are divided into ranges of
+// split_key_count(N, nsplit) keys, split_parts(N, nsplit) <= nsplit of them,
+// none empty.
+inline int split_key_count(int N, int nsplit) {
+  const int tiles = (N + 63) / 64;
+  return (tiles + nsplit - 1) / nsplit * 64;
+}
+inline int split_parts(int N, int nsplit) {
+  const int per = split_key_count(N, nsplit);
+  return (N + per - 1) / per;
+}
+
+// Partial results of every range: O parts fp32 [parts, B*H*N, d] at Op, LSE
+// parts fp32 [parts, B*H*N] at Lp.
+hipError_t launch_fwd_split(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                            const void *V, float scale, int causal, int nsplit, float *Op,
+                            float *Lp, hipStream_t stream);
+
+// O [rows, d] (dtype) and LSE [rows] from parts partial results.
+hipError_t launch_lse_merge(int dtype, int parts, long rows, int d, const float *Op,
+                            const float *Lp, void *O, float *LSE, hipStream_t stream);
+
 // D = rowsum(dO o O), fp32 [B*H*N].
 hipError_t launch_bwd_preprocess(int dtype, int B, int H, int N, int d, const void *O,
                                  const void *dO, float *Dvec, hipStream_t stream);

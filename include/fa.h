@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 /* element types */
 #define FA_F32 0
@@ -92,6 +92,54 @@ const char *fa_status_str(int status);
 int fa_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
            const void *V, float scale, int causal, void *O, float *LSE,
            void *stream);
+
+/*
+ * Split-key forward: the same O and LSE as fa_fwd (up to rounding), with
+ * the keys of every row cut into contiguous ranges that separate workgroups
+ * sweep, so that slices with few query blocks still fill the chip. Each
+ * range gives a partial result (O_s normalised by its own l_s, and LSE_s) in
+ * fp32 workspace; fa_lse_merge then folds the parts with the two-block merge
+ * of [FA] section 2, parts 3.1 and 4.1 (a part enters as (LSE_s, 1, O_s)).
+ *
+ * nsplit: 1..64 ranges at most (the key tiles of 64 keys are divided evenly
+ *   and no range is empty, so fewer may be used: fa_fwd_splitkv_parts), or 0
+ *   to let the library choose from the grid size and the current device's
+ *   compute-unit count.
+ * In/Out: as fa_fwd. dtype FA_F16 or FA_BF16 (FA_F32: FA_ERR_UNSUPPORTED).
+ * workspace: at least fa_fwd_splitkv_workspace_bytes(...) bytes, 256-byte
+ *   aligned, caller-owned, overwritten: the parts' O [parts, B, H, N, d] and
+ *   LSE [parts, B, H, N] in fp32.
+ * Enqueues two kernels (the ranges, then the merge). Deterministic.
+ */
+int fa_fwd_splitkv(int dtype, int B, int H, int N, int d, const void *Q,
+                   const void *K, const void *V, float scale, int causal,
+                   int nsplit, void *O, float *LSE, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* Workspace bytes fa_fwd_splitkv needs (0 for arguments it would reject). */
+size_t fa_fwd_splitkv_workspace_bytes(int dtype, int B, int H, int N, int d,
+                                      int nsplit);
+
+/* Number of key ranges fa_fwd_splitkv uses for this nsplit (0 if invalid). */
+int fa_fwd_splitkv_parts(int B, int H, int N, int nsplit);
+
+/*
+ * Merge of partial attention results over disjoint key sets ([FA] section 2,
+ * parts 3.1 and 4.1: the merge of two blocks' (m, l, O~), folded over the
+ * parts), for every row r:
+ *   LSE_r = log sum_s exp(LSE_sr),   O_r = sum_s exp(LSE_sr - LSE_r) O_sr.
+ * In:  O_parts fp32 [parts, rows, d] (each normalised over its own keys),
+ *      LSE_parts fp32 [parts, rows]; LSE = -inf marks an empty part.
+ * Out: O [rows, d] in dtype (FA_F32, FA_F16 or FA_BF16), LSE fp32 [rows]; a
+ *      row whose parts are all empty gets O = 0 and LSE = -inf.
+ * parts >= 1, rows >= 1, d in {64, 128}. Pointers as for the other entry
+ * points (16-byte aligned, device memory, outputs not overlapping inputs).
+ * The parts may come from fa_fwd_splitkv's workspace or from separate calls
+ * (for example one per key shard).
+ */
+int fa_lse_merge(int dtype, int parts, long long rows, int d,
+                 const float *O_parts, const float *LSE_parts, void *O,
+                 float *LSE, void *stream);
 
 /*
  * Bytes of workspace fa_bwd needs: fp32 D [B, H, N], rounded up to a

@@ -132,3 +132,49 @@ def test_binding_fails_loudly_without_gpu_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fwd(q, q, q)
+
+
+def _split(L, dtype=2, N=16, d=64, nsplit=2, ws=A, ws_bytes=None, causal=0, o=A2):
+    if ws_bytes is None:
+        ws_bytes = L.fa_fwd_splitkv_workspace_bytes(dtype, 1, 1, N, d, nsplit)
+    return L.fa_fwd_splitkv(dtype, 1, 1, N, d, A, A, A, 0.125, causal, nsplit, o, A2, ws,
+                            ws_bytes, None)
+
+
+def test_splitkv_rejects(L):
+    assert _split(L, dtype=0, ws_bytes=1 << 20) == UNSUP     # no fp32 split path
+    assert _split(L, d=96, ws_bytes=1 << 20) == UNSUP
+    assert _split(L, nsplit=-1, ws_bytes=1 << 20) == INVALID
+    assert _split(L, nsplit=65, ws_bytes=1 << 20) == INVALID
+    assert _split(L, causal=3) == INVALID
+    assert _split(L, ws=NUL) == INVALID
+    assert _split(L, o=MIS) == INVALID
+    need = L.fa_fwd_splitkv_workspace_bytes(2, 1, 1, 16, 64, 2)
+    assert need > 0
+    assert _split(L, ws_bytes=need - 1) == WS
+
+
+@pytest.mark.parametrize("N,nsplit,parts", [(1000, 4, 4), (100, 4, 2), (64, 3, 1),
+                                             (65, 64, 2), (8192, 5, 5), (8192, 64, 64)])
+def test_splitkv_parts_and_workspace(L, N, nsplit, parts):
+    """Key tiles of 64 are divided evenly over at most nsplit non-empty ranges;
+    the workspace holds every part's fp32 O and LSE."""
+    assert L.fa_fwd_splitkv_parts(2, 3, N, nsplit) == parts
+    ob = -(-parts * 2 * 3 * N * 128 * 4 // 256) * 256
+    lb = -(-parts * 2 * 3 * N * 4 // 256) * 256
+    assert L.fa_fwd_splitkv_workspace_bytes(2, 2, 3, N, 128, nsplit) == ob + lb
+    assert L.fa_fwd_splitkv_workspace_bytes(0, 2, 3, N, 128, nsplit) == 0
+    assert L.fa_fwd_splitkv_parts(2, 3, N, -1) == 0
+
+
+def test_lse_merge_rejects(L):
+    m = lambda dtype=0, parts=2, rows=10, d=64, op=A, lp=A, o=A2, lse=A2: L.fa_lse_merge(
+        dtype, parts, rows, d, op, lp, o, lse, None)
+    assert m(parts=0) == INVALID
+    assert m(rows=0) == INVALID
+    assert m(d=96) == UNSUP
+    assert m(dtype=3) == UNSUP
+    assert m(op=NUL) == INVALID
+    assert m(lp=NUL) == INVALID
+    assert m(o=MIS) == INVALID
+    assert m(lse=NUL) == INVALID
