@@ -26,6 +26,9 @@ Prints ONE JSON line. Besides the required keys it carries:
   splitkv       fa_fwd against fa_fwd_splitkv (the library's split choice) on
                 grids with fewer query blocks than the chip has workgroup
                 slots, and the merge kernel's HBM rate.
+  kvcache       fa_fwd_kvcache: decoding (one new query per slice over an
+                8192-key cache; HBM-bound, reported in GB/s of K and V read)
+                and chunked prefill (512 new queries over 8192 keys).
 """
 import argparse
 import hashlib
@@ -270,6 +273,33 @@ def splitkv_report(fa, torch, settle_s):
     return out
 
 
+def kvcache_report(fa, torch, settle_s):
+    """Attention of Nq new queries over an Nk-key cache."""
+    out = []
+    for name, B, H, Nq, Nk, causal in (("decode-b16-h32-nk8192", 16, 32, 1, 8192, True),
+                                       ("decode-b1-h32-nk32768", 1, 32, 1, 32768, True),
+                                       ("prefill-b1-h32-nq512-nk8192", 1, 32, 512, 8192, True)):
+        d = 128
+        g = torch.Generator().manual_seed(42)
+        q, k, v = (torch.randn(B, H, n, d, generator=g).to(torch.bfloat16).cuda()
+                   for n in (Nq, Nk, Nk))
+        parts = fa.fwd_kvcache_parts(B, H, Nq, Nk, 0)
+        ws = torch.empty(fa.fwd_kvcache_workspace_bytes(torch.bfloat16, B, H, Nq, Nk, d, 0),
+                         dtype=torch.uint8, device="cuda")
+        ms = _time_ms(torch, lambda: fa.fwd_kvcache(q, k, v, d ** -0.5, causal, 0, ws), 20,
+                      settle_s)
+        kv_bytes = 2 * B * H * Nk * d * 2
+        vis = Nq * Nk - (Nq * (Nq - 1)) // 2 if causal else Nq * Nk   # visible (q, k) pairs
+        flops = 4.0 * B * H * vis * d
+        out.append({"workload": name, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d,
+                    "causal": causal, "parts": parts, "ms": round(ms, 4),
+                    "kv_gbs": round(kv_bytes / ms / 1e6, 1), "tflops": round(flops / ms / 1e9, 1)})
+        print("# kvcache %s parts %d: %.4f ms, %.0f GB/s of K/V, %.1f TFLOPS" %
+              (name, parts, ms, kv_bytes / ms / 1e6, flops / ms / 1e9), file=sys.stderr,
+              flush=True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +311,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-splitkv", action="store_true")
+    ap.add_argument("--no-kvcache", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales the HBM "
                          "byte counters read under rocprofv3)")
@@ -366,6 +397,8 @@ def main():
         out["sweep"] = sweep
     if not args.no_splitkv:
         out["splitkv"] = splitkv_report(fa, torch, min(args.settle, 0.5))
+    if not args.no_kvcache:
+        out["kvcache"] = kvcache_report(fa, torch, min(args.settle, 0.5))
     print(json.dumps(out), flush=True)
 
 

@@ -14,7 +14,7 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_splitkv", "fwd_splitkv_parts", "fwd_splitkv_workspace_bytes",
-           "lse_merge", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq",
+           "fwd_kvcache", "fwd_kvcache_parts", "fwd_kvcache_workspace_bytes", "lse_merge", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq",
            "bwd_workspace_bytes", "FAError", "library_path", "lib",
            "F32", "F16", "BF16"]
 
@@ -58,6 +58,12 @@ def lib():
     L.fa_fwd_splitkv_workspace_bytes.restype = z
     L.fa_fwd_splitkv_parts.argtypes = [i, i, i, i]
     L.fa_fwd_splitkv_parts.restype = i
+    L.fa_fwd_kvcache.argtypes = [i, i, i, i, i, i, p, p, p, f, i, i, p, p, p, z, p]
+    L.fa_fwd_kvcache.restype = i
+    L.fa_fwd_kvcache_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.fa_fwd_kvcache_workspace_bytes.restype = z
+    L.fa_fwd_kvcache_parts.argtypes = [i, i, i, i, i]
+    L.fa_fwd_kvcache_parts.restype = i
     L.fa_lse_merge.argtypes = [i, i, ctypes.c_longlong, i, p, p, p, p, p]
     L.fa_lse_merge.restype = i
     L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -139,6 +145,38 @@ def fwd_splitkv(q, k, v, scale=None, causal=False, nsplit=0, workspace=None):
     _call("fa_fwd_splitkv", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _scale(scale, d),
           int(bool(causal)), int(nsplit), _ptr(o), _ptr(lse), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _stream(q))
+    return o, lse
+
+
+def fwd_kvcache_workspace_bytes(dtype, B, H, Nq, Nk, d, nsplit=0):
+    return int(lib().fa_fwd_kvcache_workspace_bytes(_CODES[dtype], B, H, Nq, Nk, d,
+                                                   int(nsplit)))
+
+
+def fwd_kvcache_parts(B, H, Nq, Nk, nsplit=0):
+    return int(lib().fa_fwd_kvcache_parts(B, H, Nq, Nk, int(nsplit)))
+
+
+def fwd_kvcache(q, k, v, scale=None, causal=True, nsplit=0, workspace=None):
+    """O, LSE of Nq new queries ([B, H, Nq, d]) over Nk cached keys and values
+    ([B, H, Nk, d]); under the causal mask query i sits at position Nk-Nq+i."""
+    for t in (q, k, v):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("expected contiguous GPU tensors [B, H, n, d] of one dtype")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d]")
+    if q.dtype not in _CODES:
+        raise ValueError("unsupported dtype %s" % q.dtype)
+    nbytes = fwd_kvcache_workspace_bytes(q.dtype, B, H, Nq, Nk, d, nsplit)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _call("fa_fwd_kvcache", _CODES[q.dtype], B, H, Nq, Nk, d, _ptr(q), _ptr(k), _ptr(v),
+          _scale(scale, d), int(bool(causal)), int(nsplit), _ptr(o), _ptr(lse),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
     return o, lse
 
 

@@ -48,33 +48,62 @@ constexpr int kMaxSplit = 64;
 // two, with at least 16 key tiles per range (shorter ranges do not repay the
 // extra kernel and the merge: at B2 H8 N1024 two ranges of 8 tiles ran
 // 0.017 ms and four of 4 tiles 0.022 ms, against 0.015 ms unsplit).
-int auto_split(int B, int H, int N) {
+int auto_split(int B, int H, int Nq, int Nk) {
   int cus = 256, dev = 0, v = 0;
   if (hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
     cus = v;
-  const long units = (long)B * H * ((N + 127) / 128);
+  const long units = (long)B * H * ((Nq + 127) / 128);
   long ns = (2L * cus + units - 1) / units;
-  const long tiles = (N + 63) / 64;
+  const long tiles = (Nk + 63) / 64;
   if (ns > tiles / 16) ns = tiles / 16;
   if (ns > kMaxSplit) ns = kMaxSplit;
   return ns < 1 ? 1 : (int)ns;
 }
 
 // Requested split count -> ranges actually used (0 if invalid).
-int resolve_split(int B, int H, int N, int nsplit) {
+int resolve_split(int B, int H, int Nq, int Nk, int nsplit) {
   if (nsplit < 0 || nsplit > kMaxSplit) return 0;
-  if (nsplit == 0) nsplit = auto_split(B, H, N);
-  return fa::split_parts(N, nsplit);
+  if (nsplit == 0) nsplit = auto_split(B, H, Nq, Nk);
+  return fa::split_parts(Nk, nsplit);
 }
 
-// Workspace of the split forward for `parts` ranges: O parts, then LSE parts.
-size_t split_o_bytes(int parts, int B, int H, int N, int d) {
-  return round_up((size_t)parts * B * H * N * d * sizeof(float), kWsAlign);
+// Workspace of the split forward for `parts` ranges and Nq query rows per
+// slice: O parts, then LSE parts.
+size_t split_o_bytes(int parts, int B, int H, int Nq, int d) {
+  return round_up((size_t)parts * B * H * Nq * d * sizeof(float), kWsAlign);
 }
-size_t split_bytes(int parts, int B, int H, int N, int d) {
-  return split_o_bytes(parts, B, H, N, d) +
-         round_up((size_t)parts * B * H * N * sizeof(float), kWsAlign);
+size_t split_bytes(int parts, int B, int H, int Nq, int d) {
+  return split_o_bytes(parts, B, H, Nq, d) +
+         round_up((size_t)parts * B * H * Nq * sizeof(float), kWsAlign);
+}
+
+// Shape checks of the cached-prefix forward: Nq new queries over Nk keys.
+int check_kv_shape(int dtype, int B, int H, int Nq, int Nk, int d, int causal) {
+  int rc = check_shape(dtype, B, H, Nq, d, false);
+  if (rc != FA_OK) return rc;
+  if ((rc = check_shape(dtype, B, H, Nk, d, false)) != FA_OK) return rc;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (causal == 1 && Nq > Nk) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+// The split-key forward of Nq queries over Nk keys (Nq = Nk for the plain
+// case), then the merge; arguments already checked except the workspace.
+int run_split(int dtype, int B, int H, int Nq, int Nk, int d, const void *Q, const void *K,
+              const void *V, float scale, int causal, int nsplit, void *O, float *LSE,
+              void *workspace, size_t workspace_bytes, void *stream) {
+  if (nsplit < 0 || nsplit > kMaxSplit) return FA_ERR_INVALID_ARG;
+  const int req = nsplit == 0 ? auto_split(B, H, Nq, Nk) : nsplit;
+  const int parts = fa::split_parts(Nk, req);
+  if (workspace_bytes < split_bytes(parts, B, H, Nq, d)) return FA_ERR_WORKSPACE;
+  float *Op = (float *)workspace;
+  float *Lp = (float *)((char *)workspace + split_o_bytes(parts, B, H, Nq, d));
+  hipStream_t st = (hipStream_t)stream;
+  int rc = status(
+      fa::launch_fwd_split(dtype, B, H, Nq, Nk, d, Q, K, V, scale, causal, req, Op, Lp, st));
+  if (rc != FA_OK) return rc;
+  return status(fa::launch_lse_merge(dtype, parts, (long)B * H * Nq, d, Op, Lp, O, LSE, st));
 }
 
 }  // namespace
@@ -107,14 +136,40 @@ int fa_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, 
 
 size_t fa_fwd_splitkv_workspace_bytes(int dtype, int B, int H, int N, int d, int nsplit) {
   if (check_shape(dtype, B, H, N, d, false) != FA_OK || dtype == FA_F32) return 0;
-  const int parts = resolve_split(B, H, N, nsplit);
+  const int parts = resolve_split(B, H, N, N, nsplit);
   if (parts == 0) return 0;
   return split_bytes(parts, B, H, N, d);
 }
 
 int fa_fwd_splitkv_parts(int B, int H, int N, int nsplit) {
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return resolve_split(B, H, N, nsplit);
+  return resolve_split(B, H, N, N, nsplit);
+}
+
+size_t fa_fwd_kvcache_workspace_bytes(int dtype, int B, int H, int Nq, int Nk, int d,
+                                      int nsplit) {
+  if (check_kv_shape(dtype, B, H, Nq, Nk, d, 0) != FA_OK) return 0;
+  const int parts = resolve_split(B, H, Nq, Nk, nsplit);
+  if (parts == 0) return 0;
+  return split_bytes(parts, B, H, Nq, d);
+}
+
+int fa_fwd_kvcache_parts(int B, int H, int Nq, int Nk, int nsplit) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0) return 0;
+  return resolve_split(B, H, Nq, Nk, nsplit);
+}
+
+int fa_fwd_kvcache(int dtype, int B, int H, int Nq, int Nk, int d, const void *Q, const void *K,
+                   const void *V, float scale, int causal, int nsplit, void *O, float *LSE,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_kv_shape(dtype, B, H, Nq, Nk, d, causal);
+  if (rc != FA_OK) return rc;
+  if ((rc = check_scale_causal(scale, causal)) != FA_OK) return rc;
+  if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O) || !vec_ok(LSE) ||
+      !tensor_ok(workspace))
+    return FA_ERR_INVALID_ARG;
+  return run_split(dtype, B, H, Nq, Nk, d, Q, K, V, scale, causal, nsplit, O, LSE, workspace,
+                   workspace_bytes, stream);
 }
 
 int fa_lse_merge(int dtype, int parts, long long rows, int d, const float *O_parts,
@@ -140,18 +195,8 @@ int fa_fwd_splitkv(int dtype, int B, int H, int N, int d, const void *Q, const v
   if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O) || !vec_ok(LSE) ||
       !tensor_ok(workspace))
     return FA_ERR_INVALID_ARG;
-  if (nsplit < 0 || nsplit > kMaxSplit) return FA_ERR_INVALID_ARG;
-  const int req = nsplit == 0 ? auto_split(B, H, N) : nsplit;
-  const int parts = fa::split_parts(N, req);
-  if (workspace_bytes < split_bytes(parts, B, H, N, d)) return FA_ERR_WORKSPACE;
-  float *Op = (float *)workspace;
-  float *Lp = (float *)((char *)workspace + split_o_bytes(parts, B, H, N, d));
-  hipStream_t st = (hipStream_t)stream;
-  if ((rc = status(fa::launch_fwd_split(dtype, B, H, N, d, Q, K, V, scale, causal, req, Op, Lp,
-                                        st))) != FA_OK)
-    return rc;
-  return status(
-      fa::launch_lse_merge(dtype, parts, (long)B * H * N, d, Op, Lp, O, LSE, st));
+  return run_split(dtype, B, H, N, N, d, Q, K, V, scale, causal, nsplit, O, LSE, workspace,
+                   workspace_bytes, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d) {

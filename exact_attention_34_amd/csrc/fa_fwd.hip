@@ -78,8 +78,11 @@ __device__ __forceinline__ int swz_v(int row) {
 // loaded two tiles ahead and V tiles one tile ahead.
 //
 // One block of BR query rows (block qb of slice bh) against the keys in
-// [kfirst, klim) (kfirst a multiple of BC; the whole row is [0, N)); K0, K1,
-// V0, V1 are the workgroup's LDS tiles. PART = false writes O (in T,
+// [kfirst, klim) (kfirst a multiple of BC; the whole row is [0, Nk)). The
+// slice has Nq queries and Nk keys; query i sits at position qoff + i, which
+// the causal mask compares with the key index (qoff = 0 when Nq = Nk, and
+// Nk - Nq for new queries appended to a cached prefix). K0, K1, V0, V1 are
+// the workgroup's LDS tiles. PART = false writes O (in T,
 // normalised) and LSE; PART = true writes the partial result of this key
 // range in fp32 to Op / Lp: O~ / l and m + log l, or 0 and -inf for a row
 // that sees none of these keys.
@@ -88,7 +91,8 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
                                           const uint16_t *__restrict__ K,
                                           const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
                                           float *__restrict__ LSE, float *__restrict__ Op,
-                                          float *__restrict__ Lp, int N, int bh, int qb,
+                                          float *__restrict__ Lp, int Nq, int Nk, int qoff,
+                                          int bh, int qb,
                                           int kfirst, int klim, float c2, uint16_t *K0,
                                           uint16_t *K1, uint16_t *V0, uint16_t *V1) {
   using C = FwdCfg<D>;
@@ -98,17 +102,18 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
   const int q0 = qb * C::BR;
   const int wq0 = q0 + 32 * w;  // first query row of this wave
   const int qrow = wq0 + l32;
-  const size_t base = (size_t)bh * N * D;
-  const uint16_t *Qh = Q + base, *Kh = K + base, *Vh = V + base;
+  const size_t base = (size_t)bh * Nq * D;   // Q, O rows of this slice
+  const size_t kvbase = (size_t)bh * Nk * D;  // K, V rows
+  const uint16_t *Qh = Q + base, *Kh = K + kvbase, *Vh = V + kvbase;
 
-  // Rows and keys past N are read from row N - 1 (clamped, always valid
-  // memory): their queries are never stored and their keys are masked.
+  // Rows past Nq are read from row Nq - 1 (clamped, always valid memory) and
+  // never stored; keys past the range are masked.
   u32x4 qreg[C::NCH];
-  const int qld = min(qrow, N - 1);
+  const int qld = min(qrow, Nq - 1);
 #pragma unroll
   for (int c = 0; c < C::NCH; ++c) qreg[c] = ld128(Qh + (size_t)qld * D + 16 * c + 8 * g);
 
-  const int kend = CAUSAL ? min(klim, q0 + C::BR) : klim;
+  const int kend = CAUSAL ? min(klim, qoff + q0 + C::BR) : klim;
   const int ntiles = max(kend - kfirst + C::BC - 1, 0) / C::BC;
 
   // Direct buffer -> LDS loads: instruction i of wave w fills LDS chunks
@@ -128,7 +133,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
   auto tile_rsrc = [&](const uint16_t *src, int kt) __attribute__((always_inline)) {
     const int kb = kfirst + kt * C::BC;
     const int rows = max(min(kend - kb, C::BC), 0);
-    return make_rsrc(src + (size_t)min(kb, N) * D, (uint32_t)rows * D * 2);
+    return make_rsrc(src + (size_t)min(kb, Nk) * D, (uint32_t)rows * D * 2);
   };
   // Load i of this wave for tile kt of one tensor into the LDS tile dst.
   auto dma = [&](const i32x4 &rs, const int (&go)[C::LPW], uint16_t *dst, int i)
@@ -230,9 +235,9 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
     __builtin_amdgcn_sched_barrier(0);
     s_mfma(sn, Kn, 0);
     __builtin_amdgcn_sched_barrier(0);
-    if ((kb + C::BC > klim) || (CAUSAL && kb + C::BC - 1 > wq0)) {
+    if ((kb + C::BC > klim) || (CAUSAL && kb + C::BC - 1 > qoff + wq0)) {
       // Key kb + 4g + off is visible iff off <= lim (one compare per score).
-      const int lim = (CAUSAL ? min(qrow, klim - 1) : klim - 1) - kb - 4 * g;
+      const int lim = (CAUSAL ? min(qoff + qrow, klim - 1) : klim - 1) - kb - 4 * g;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -324,6 +329,22 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
   }
   wait_vmem_all();
   __syncthreads();
+  if (PART && wq0 >= Nq) {
+    // None of this wave's rows exists (few queries, as in decoding): it only
+    // issues its share of the tile loads and meets every barrier.
+    for (int kt = 0; kt < ntiles; ++kt) {
+      const int b = kt & 1;
+      wait_vmem_all();
+      __syncthreads();
+      const i32x4 krs = tile_rsrc(Kh, kt + 2), vrs = tile_rsrc(Vh, kt + 1);
+#pragma unroll
+      for (int i = 0; i < C::LPW; ++i) {
+        dma(krs, gk, kbuf(b), i);
+        dma(vrs, gv, vbuf(b ^ 1), i);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < C::NCH; ++c) s_mfma(sa, kbuf(0), c);
   for (int kt = 0; kt < ntiles; kt += 2) {
@@ -336,7 +357,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
   const float l_tot = pair_sum(l_run);
   const float inv = fast_rcp(l_tot);
   if (PART) {
-    if (qrow < N) {
+    if (qrow < Nq) {
       const bool any = l_tot > 0.f;
       const float f = any ? inv : 0.f;
       float *Orow = Op + base + (size_t)qrow * D;
@@ -349,11 +370,11 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
           *(f32x4 *)(Orow + 32 * dt + 8 * i + 4 * g) = v;
         }
       if (g == 0)
-        Lp[(size_t)bh * N + qrow] = any ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+        Lp[(size_t)bh * Nq + qrow] = any ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
     }
     return;
   }
-  if (qrow < N) {
+  if (qrow < Nq) {
     uint16_t *Orow = O + base + (size_t)qrow * D;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
@@ -364,7 +385,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
         v[1] = pack2<T>(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
         *(u32x2 *)(Orow + 32 * dt + 8 * i + 4 * g) = v;
       }
-    if (g == 0) LSE[(size_t)bh * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+    if (g == 0) LSE[(size_t)bh * Nq + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
   }
 }
 
@@ -388,30 +409,30 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void
   const int bh = tile / nunits;
   const int u = tile - bh * nunits;
   if (!CAUSAL) {
-    fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, bh, u, 0, N, c2, K0, K1,
-                                   V0, V1);
+    fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, u, 0, N, c2,
+                                   K0, K1, V0, V1);
     return;
   }
-  fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, bh, nqb - 1 - u, 0, N, c2,
-                                 K0, K1, V0, V1);
+  fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, nqb - 1 - u, 0,
+                                 N, c2, K0, K1, V0, V1);
   if (u != nqb - 1 - u) {
     __syncthreads();  // every wave is done with the LDS tiles
-    fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, bh, u, 0, N, c2, K0, K1,
-                                   V0, V1);
+    fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, u, 0, N, c2,
+                                   K0, K1, V0, V1);
   }
 }
 
 // Split-key forward: the keys of every row are cut into nsplit ranges of
 // split_keys keys (a multiple of the tile width), and each (slice, range,
 // query block) is one workgroup, which writes its partial result in fp32:
-// part s of slice bh at Op + (s * BH + bh) * N * D and Lp + (s * BH + bh) * N.
+// part s of slice bh at Op + (s * BH + bh) * Nq * D and Lp + (s * BH + bh) * Nq.
 // Workgroups of one slice and range are consecutive, so they share their K
 // and V tiles in one L2. The partials are combined by lse_merge_kernel.
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void fwd_split_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, float *__restrict__ Op, float *__restrict__ Lp, int N,
-    int BH, int nqb, int nsplit, int split_keys, int total, float c2) {
+    const uint16_t *__restrict__ V, float *__restrict__ Op, float *__restrict__ Lp, int Nq,
+    int Nk, int qoff, int BH, int nqb, int nsplit, int split_keys, int total, float c2) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t K0[C::TILE], K1[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t V0[C::TILE], V1[C::TILE];
@@ -421,10 +442,10 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void
   const int r = tile - bh * per_bh;
   const int sp = r / nqb, qb = r - sp * nqb;
   const int kfirst = sp * split_keys;
-  const int klim = min(N, kfirst + split_keys);
+  const int klim = min(Nk, kfirst + split_keys);
   const size_t part = (size_t)sp * BH;
-  fwd_block<T, D, CAUSAL, true>(Q, K, V, nullptr, nullptr, Op + part * N * D, Lp + part * N, N,
-                                bh, qb, kfirst, klim, c2, K0, K1, V0, V1);
+  fwd_block<T, D, CAUSAL, true>(Q, K, V, nullptr, nullptr, Op + part * Nq * D, Lp + part * Nq,
+                                Nq, Nk, qoff, bh, qb, kfirst, klim, c2, K0, K1, V0, V1);
 }
 
 // Merge of partial results over disjoint key sets, per row r and part s:
@@ -640,39 +661,38 @@ static hipError_t fwd_b16_c(int causal, int BH, int N, const void *Q, const void
                 : fwd_b16<T, D, false>(BH, N, Q, K, V, c2, O, LSE, st);
 }
 
+struct SplitArgs {
+  int BH, Nq, Nk, qoff;
+  const void *Q, *K, *V;
+  float c2;
+  float *Op, *Lp;
+  int nsplit, split_keys;
+};
+
 template <typename T, int D, bool CAUSAL>
-static hipError_t fwd_split(int BH, int N, const void *Q, const void *K, const void *V, float c2,
-                            float *Op, float *Lp, int nsplit, int split_keys, hipStream_t st) {
+static hipError_t fwd_split(const SplitArgs &a, hipStream_t st) {
   using C = FwdCfg<D>;
-  const int nqb = (N + C::BR - 1) / C::BR;
-  const int total = BH * nsplit * nqb;
+  const int nqb = (a.Nq + C::BR - 1) / C::BR;
+  const int total = a.BH * a.nsplit * nqb;
   hipLaunchKernelGGL((fwd_split_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
-                     (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, Op, Lp, N, BH,
-                     nqb, nsplit, split_keys, total, c2);
+                     (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V, a.Op,
+                     a.Lp, a.Nq, a.Nk, a.qoff, a.BH, nqb, a.nsplit, a.split_keys, total, a.c2);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t fwd_split_c(int causal, int BH, int N, const void *Q, const void *K,
-                              const void *V, float c2, float *Op, float *Lp, int nsplit,
-                              int split_keys, hipStream_t st) {
-  return causal ? fwd_split<T, D, true>(BH, N, Q, K, V, c2, Op, Lp, nsplit, split_keys, st)
-                : fwd_split<T, D, false>(BH, N, Q, K, V, c2, Op, Lp, nsplit, split_keys, st);
+static hipError_t fwd_split_c(int causal, const SplitArgs &a, hipStream_t st) {
+  return causal ? fwd_split<T, D, true>(a, st) : fwd_split<T, D, false>(a, st);
 }
 
-hipError_t launch_fwd_split(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
-                            const void *V, float scale, int causal, int nsplit, float *Op,
-                            float *Lp, hipStream_t st) {
-  const int BH = B * H;
-  const float c2 = scale * kLog2e;
-  const int split_keys = split_key_count(N, nsplit);
-  const int parts = split_parts(N, nsplit);
+hipError_t launch_fwd_split(int dtype, int B, int H, int Nq, int Nk, int d, const void *Q,
+                            const void *K, const void *V, float scale, int causal, int nsplit,
+                            float *Op, float *Lp, hipStream_t st) {
+  const SplitArgs a{B * H, Nq, Nk, causal ? Nk - Nq : 0, Q, K, V, scale * kLog2e, Op, Lp,
+                    split_parts(Nk, nsplit), split_key_count(Nk, nsplit)};
   if (dtype == kBF16)
-    return d == 64 ? fwd_split_c<BF16, 64>(causal, BH, N, Q, K, V, c2, Op, Lp, parts, split_keys, st)
-                   : fwd_split_c<BF16, 128>(causal, BH, N, Q, K, V, c2, Op, Lp, parts, split_keys,
-                                            st);
-  return d == 64 ? fwd_split_c<F16, 64>(causal, BH, N, Q, K, V, c2, Op, Lp, parts, split_keys, st)
-                 : fwd_split_c<F16, 128>(causal, BH, N, Q, K, V, c2, Op, Lp, parts, split_keys, st);
+    return d == 64 ? fwd_split_c<BF16, 64>(causal, a, st) : fwd_split_c<BF16, 128>(causal, a, st);
+  return d == 64 ? fwd_split_c<F16, 64>(causal, a, st) : fwd_split_c<F16, 128>(causal, a, st);
 }
 
 hipError_t launch_lse_merge(int dtype, int parts, long rows, int d, const float *Op,

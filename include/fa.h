@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 /* element types */
 #define FA_F32 0
@@ -122,6 +122,31 @@ size_t fa_fwd_splitkv_workspace_bytes(int dtype, int B, int H, int N, int d,
 
 /* Number of key ranges fa_fwd_splitkv uses for this nsplit (0 if invalid). */
 int fa_fwd_splitkv_parts(int B, int H, int N, int nsplit);
+
+/*
+ * Forward of Nq new queries over Nk keys, for streaming use of the online
+ * softmax over a cached prefix ([FA] section 2, part 7: the same running
+ * (m, l, O~) lets keys arrive in pieces and be cached): token-by-token
+ * decoding (Nq = 1) and chunked prefill (Nq > 1). Query i of a slice sits at
+ * position Nk - Nq + i, so with causal = 1 it sees keys 0 .. Nk - Nq + i (the
+ * cached prefix and the new keys up to itself; requires Nq <= Nk). With
+ * causal = 0 every query sees all Nk keys (any Nq).
+ * In:  Q [B, H, Nq, d], K and V [B, H, Nk, d] dtype (FA_F16 or FA_BF16).
+ * Out: O [B, H, Nq, d] dtype, LSE [B, H, Nq] fp32.
+ * Runs as fa_fwd_splitkv does (key ranges swept by separate workgroups, then
+ * fa_lse_merge); nsplit and workspace as there, with its own size function.
+ */
+int fa_fwd_kvcache(int dtype, int B, int H, int Nq, int Nk, int d,
+                   const void *Q, const void *K, const void *V, float scale,
+                   int causal, int nsplit, void *O, float *LSE,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes fa_fwd_kvcache needs (0 for arguments it would reject). */
+size_t fa_fwd_kvcache_workspace_bytes(int dtype, int B, int H, int Nq, int Nk,
+                                      int d, int nsplit);
+
+/* Number of key ranges fa_fwd_kvcache uses for this nsplit (0 if invalid). */
+int fa_fwd_kvcache_parts(int B, int H, int Nq, int Nk, int nsplit);
 
 /*
  * Merge of partial attention results over disjoint key sets ([FA] section 2,

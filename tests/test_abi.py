@@ -178,3 +178,29 @@ def test_lse_merge_rejects(L):
     assert m(lp=NUL) == INVALID
     assert m(o=MIS) == INVALID
     assert m(lse=NUL) == INVALID
+
+
+def test_kvcache_rejects(L):
+    k = lambda dtype=2, Nq=4, Nk=100, d=64, causal=1, nsplit=0, ws=A, nb=1 << 24, o=A2: \
+        L.fa_fwd_kvcache(dtype, 1, 2, Nq, Nk, d, A, A, A, 0.125, causal, nsplit, o, A2, ws, nb,
+                         None)
+    assert k(Nq=101) == INVALID          # causal needs Nq <= Nk
+    assert k(Nq=0) == INVALID and k(Nk=0) == INVALID
+    assert k(dtype=0) == UNSUP and k(d=80) == UNSUP
+    assert k(nsplit=65) == INVALID
+    assert k(ws=NUL) == INVALID and k(o=MIS) == INVALID
+    assert k(nb=16) == WS
+    assert L.fa_fwd_kvcache_workspace_bytes(2, 1, 2, 4, 100, 64, 2) > 0
+    assert L.fa_fwd_kvcache_workspace_bytes(0, 1, 2, 4, 100, 64, 2) == 0
+    # Nq > Nk is allowed without the mask (every query sees every key)
+    assert L.fa_fwd_kvcache_workspace_bytes(2, 1, 2, 300, 100, 64, 2) > 0
+
+
+@pytest.mark.parametrize("Nq,Nk,nsplit,parts", [(1, 8192, 8, 8), (7, 100, 4, 2), (512, 8192, 3, 3)])
+def test_kvcache_parts_and_workspace(L, Nq, Nk, nsplit, parts):
+    """Ranges are cut from the Nk keys; the workspace holds fp32 O and LSE for
+    the Nq query rows of every part."""
+    assert L.fa_fwd_kvcache_parts(2, 3, Nq, Nk, nsplit) == parts
+    ob = -(-parts * 6 * Nq * 128 * 4 // 256) * 256
+    lb = -(-parts * 6 * Nq * 4 // 256) * 256
+    assert L.fa_fwd_kvcache_workspace_bytes(2, 2, 3, Nq, Nk, 128, nsplit) == ob + lb

@@ -450,3 +450,20 @@ def test_lse_merge_ignores_empty_parts_and_order(oracle_lib):
     assert np.array_equal(lse1, lse_parts[0])
     o0, lse0 = oracle_lib.lse_merge(junk, np.full((1, N), -np.inf))
     assert np.all(o0 == 0.0) and np.all(lse0 == -np.inf)
+
+
+def test_rows_at_offset_positions_equal_prefix_attention(oracle_lib):
+    """Queries appended after a cached prefix (query i at position Nk - Nq + i)
+    under the causal mask: each equals unmasked attention over the keys up to
+    its position, and the last one sees every key."""
+    rng = _rng(31)
+    Nq, Nk, d = 5, 23, 4
+    q = rng.standard_normal((Nq, d)); k = rng.standard_normal((Nk, d))
+    v = rng.standard_normal((Nk, d))
+    pos = np.arange(Nq) + Nk - Nq
+    o, lse = oracle_lib.attention_fwd_rows(q, pos, k, v, 0.7, True)
+    for i, p in enumerate(pos):
+        oi, li = oracle_lib.attention_fwd_rows(q[i:i + 1], [Nk], k[:p + 1], v[:p + 1], 0.7, False)
+        assert np.allclose(oi[0], o[i], rtol=0, atol=1e-14)
+        assert abs(li[0] - lse[i]) <= 1e-14
+    assert pos[-1] == Nk - 1
