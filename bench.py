@@ -53,18 +53,19 @@ def _src_hash(path):
 
 def _traffic(kernel, workload):
     """Per-launch HBM bytes of a kernel from the committed counter summary, or
-    None if absent, taken on another workload, or taken on other kernel
-    source (every file it lists must hash the same)."""
+    None if absent, taken on another workload, or taken on other source of
+    that kernel (every file listed for it must hash the same)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         if t.get("workload") != workload:
             return None
-        if any(_src_hash(p) != h for p, h in t["sources"].items()):
+        k = t["kernels"][kernel]
+        if any(_src_hash(p) != h for p, h in k["sources"].items()):
             return None
+        return k["bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         return None
-    return t.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
 
 def _inputs(w, torch, dev):
