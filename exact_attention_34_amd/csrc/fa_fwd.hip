@@ -206,7 +206,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
   // Vector instructions placed after each MFMA of phase A and of phase B
   // (about the same vector work per tile for both head sizes, half the
   // MFMAs for d = 64).
-  constexpr int kValuA = (D == 128) ? 6 : 14;
+  constexpr int kValuA = (D == 128) ? 5 : 14;
   constexpr int kValuB = (D == 128) ? 4 : 7;
   // MFMAs of phase A (after the first NT) and of phase B; MFMAs between two
   // direct loads in each.
