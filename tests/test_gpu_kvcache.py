@@ -37,6 +37,9 @@ CASES = [(dt, d, causal, Nq, Nk, ns) for dt, d in (("bf16", 128), ("f16", 64))
          for causal in (False, True)
          for Nq, Nk, ns in ((1, 1, 0), (1, 777, 0), (1, 4096, 8), (7, 300, 2), (128, 1000, 3),
                             (200, 200, 0), (300, 5000, 0))]
+# without the mask the query count is free: more new queries than keys
+CASES += [(dt, d, False, Nq, Nk, ns) for dt, d in (("bf16", 128), ("f16", 64))
+          for Nq, Nk, ns in ((300, 70, 0), (129, 64, 2))]
 
 
 @pytest.mark.parametrize("dt,d,causal,Nq,Nk,nsplit", CASES)
