@@ -22,7 +22,9 @@ Prints ONE JSON line. Besides the required keys it carries:
   cpu_baseline  the fp64 oracle timed on host cores on a sample of the same
                 workload (also used as a parity spot-check of the timed run);
   sweep         forward and forward+backward TFLOPS for bf16 d = 128 at
-                N = 2048, 4096, 8192 (B*N = 16384 tokens, 16 heads).
+                N = 2048, 4096, 8192 (B*N = 16384 tokens, 16 heads), causal
+                and not, and for the workloads B4 H32 N2048 d128 bf16 and
+                B1 H16 N8192 d64 fp16 causal.
   splitkv       fa_fwd against fa_fwd_splitkv (the library's split choice) on
                 grids with fewer query blocks than the chip has workgroup
                 slots, and the merge kernel's HBM rate.
@@ -382,14 +384,14 @@ def main():
     if not args.no_sweep:
         sweep = []
         for name in ("perf-2k", "perf-4k", "perf-8k", "perf-2k-causal", "perf-4k-causal",
-                     "perf-8k-causal"):
+                     "perf-8k-causal", "c3", "c4"):
             ws = ai.WORKLOADS[name]
             s_ms, f_ms, _, _, _ = time_workload(fa, torch, ws, 10, 3, per_kernel=False,
                                                   settle_s=min(args.settle, 0.5))
             tf = (ws.fwd_flops() + ws.bwd_flops()) / (s_ms * 1e-3) / 1e12
             ff = ws.fwd_flops() / (f_ms * 1e-3) / 1e12
-            sweep.append({"workload": name, "B": ws.B, "H": ws.H, "N": ws.N,
-                          "causal": ws.causal, "fwd_tflops": round(ff, 1),
+            sweep.append({"workload": name, "B": ws.B, "H": ws.H, "N": ws.N, "d": ws.d,
+                          "dtype": ws.dtype, "causal": ws.causal, "fwd_tflops": round(ff, 1),
                           "fwdbwd_tflops": round(tf, 1),
                           "fwd_frac": round(ff / PEAK_BF16_TFLOPS, 4),
                           "fwdbwd_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
