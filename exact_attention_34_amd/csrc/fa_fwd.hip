@@ -16,8 +16,9 @@
 //   * Q rows stay in VGPRs for the whole sweep, as the B operand of
 //     S^T = K Q^T (v_mfma_f32_32x32x16_{bf16,f16}); lane l owns query row
 //     l % 32, so a row's 64 tile scores sit in two lanes (l and l ^ 32).
-//   * Row max and row sum are in-register reductions plus one
-//     v_permlane32_swap between the wave halves.
+//   * The row sum is an in-register reduction plus one v_permlane32_swap
+//     between the wave halves (at the end of the sweep). The row max is
+//     formed only when the reference m has to move (see below).
 //   * P, rounded to the input type, is the B operand of O~^T += V^T P^T
 //     straight from registers; the V^T operand is read from the row-major V
 //     tile with transposing LDS reads (ds_read_b64_tr_b16).
@@ -34,9 +35,6 @@
 #include "fa_launch.h"
 
 namespace fa {
-
-// Slack of the running reference max (base-2 units): P <= 2^kMaxSlack.
-constexpr float kMaxSlack = 8.f;
 
 template <int D>
 struct FwdCfg {
@@ -72,10 +70,20 @@ __device__ __forceinline__ int swz_v(int row) {
   return (4 * (row >> C::SH)) & (C::CPR - 4);
 }
 
-// The sweep is software-pipelined by one tile: while the softmax of tile j
-// runs on the vector ALUs, the matrix cores already compute the scores of
-// tile j + 1, so that each wave keeps both busy. K tiles are therefore
-// loaded two tiles ahead and V tiles one tile ahead.
+// The sweep is software-pipelined: step j takes the exponentials of tile j
+// on the vector ALUs while the matrix cores run the P V products of tile
+// j - 1 and the scores of tile j + 1, so that each wave keeps both busy. K
+// tiles are loaded two tiles ahead, V tiles one step before their use.
+//
+// Reference max. Any reference m gives the same O~ / l (the merges above
+// hold for any m that is shared by O~ and l), so m only has to keep P finite
+// and inside the 16-bit range. Step j therefore first takes P = 2^(s c2 - m)
+// against the current m and keeps it when each lane's sum of its P values is
+// at most kSumMax (every P is then at most kSumMax). Only otherwise -- and
+// for a row's first tile -- does m move to the row max: the scores are
+// formed again from K in global memory (the LDS tile is being refilled), O~
+// and l are rescaled and P recomputed. With scores that are not adversarial
+// this is a handful of tiles per row, and the common step forms no max.
 //
 // One block of BR query rows (block qb of slice bh) against the keys in
 // [kfirst, klim) (kfirst a multiple of BC; the whole row is [0, Nk)). The
@@ -165,7 +173,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
   for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m_run = -INFINITY;  // running reference max of scaled scores (base-2 units)
+  float m_run = -INFINITY;  // reference: the row max when it last moved (base-2 units)
   float l_run = 0.f;        // this lane's share of the running normaliser
 
   constexpr int NT = C::NT;
@@ -203,40 +211,50 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
     }
   };
 
-  // Vector instructions placed after each MFMA of phase A and of phase B
-  // (about the same vector work per tile for both head sizes, half the
-  // MFMAs for d = 64).
-  constexpr int kValuA = (D == 128) ? 5 : 14;
-  constexpr int kValuB = (D == 128) ? 4 : 7;
-  // MFMAs of phase A (after the first NT) and of phase B; MFMAs between two
-  // direct loads in each.
-  constexpr int kMfmaA = NT * C::NCH - NT, kMfmaB = 2 * NT * C::NDT;
-  constexpr int kDmaGapA = kMfmaA / C::LPW;
-  constexpr int kDmaGapB = kMfmaB / C::LPW;
-  // Exponential chunks (subtile t, 16-key chunk cc) in phase A: the first
-  // half; the rest in phase B.
-  constexpr int kChunksA = NT;
+  // A step has two parts: the previous tile's P V MFMAs (kMfmaP), then the
+  // next tile's S MFMAs (kMfmaS), each with half of this tile's
+  // exponentials: kValu1 / kValu2 vector instructions after each MFMA, and a
+  // direct load every kDmaGap MFMAs (V loads in the first part, K in the
+  // second).
+  constexpr int kMfmaS = NT * C::NCH, kMfmaP = 2 * NT * C::NDT;
+  constexpr int kValu1 = (D == 128) ? 3 : 8, kValu2 = (D == 128) ? 4 : 8;
+  constexpr int kDmaGap1 = kMfmaP / C::LPW, kDmaGap2 = kMfmaS / C::LPW;
+  // Bound on each lane's sum of P against the current reference (below the
+  // fp16 maximum, 65504).
+  constexpr float kSumMax = 32768.f;
 
-  // One tile kt: s holds its scores (already issued), sn receives those of
-  // tile kt + 1 (from K buffer b ^ 1; past the last tile the result is
-  // unused). V of tile kt is in V buffer b.
-  auto step = [&](int kt, f32x16 (&s)[NT], f32x16 (&sn)[NT], int b) __attribute__((always_inline)) {
-    const int kb = kfirst + kt * C::BC;
-    // Every wave's loads of K (kt + 1) and V (kt) have landed, and every wave
-    // is done with K buffer b (read for tile kt) and V buffer b ^ 1, which
-    // receive K (kt + 2) in phase A and V (kt + 1) in phase B.
-    wait_vmem_all();
-    __syncthreads();
-    const uint16_t *Kn = kbuf(b ^ 1), *Vs = vbuf(b);
-    const i32x4 krs = tile_rsrc(Kh, kt + 2), vrs = tile_rsrc(Vh, kt + 1);
+  // Reference update for the scores s of one tile (a uniform branch, taken
+  // for a row's first tile and when P would outgrow kSumMax): m moves to the
+  // row max, O~ and l are rescaled, P and its sum are recomputed.
+  auto rebase = [&](f32x16 (&s)[NT], u32x4 (&pc)[2 * NT], float &psum)
+      __attribute__((always_inline)) {
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[t][r]);
+    mloc = pair_max(mloc);
+    const float m_cand = fmaxf(m_run, mloc * c2);
+    if (m_cand > m_run) {
+      const float alpha = fast_exp2(m_run - m_cand);
+      m_run = m_cand;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    const float mb = (m_run == -INFINITY) ? 0.f : m_run;
+    psum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2 * NT; ++k) pc[k] = p_chunk(s[k / 2], k % 2, mb, psum);
+  };
 
-    // Phase A: the next tile's S MFMAs, with this tile's mask, row max,
-    // reference update and the first half of its exponentials in between.
-    __builtin_amdgcn_sched_barrier(0);
-    s_mfma(sn, Kn, 0);
-    __builtin_amdgcn_sched_barrier(0);
+  // Scores of keys past the range or (causal) after the row's position
+  // become -inf. Key kb + 4g + off is visible iff off <= lim (one compare
+  // per score).
+  auto apply_mask = [&](f32x16 (&s)[NT], int kb) __attribute__((always_inline)) {
     if ((kb + C::BC > klim) || (CAUSAL && kb + C::BC - 1 > qoff + wq0)) {
-      // Key kb + 4g + off is visible iff off <= lim (one compare per score).
       const int lim = (CAUSAL ? min(qoff + qrow, klim - 1) : klim - 1) - kb - 4 * g;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
@@ -244,86 +262,112 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
         for (int r = 0; r < 16; ++r)
           if (32 * t + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = -INFINITY;
     }
+  };
+
+  // Scores of tile kt again, from K in global memory (the tile's LDS buffer
+  // is being refilled): rows past Nk read row Nk - 1 and are masked.
+  auto rescore = [&](f32x16 (&sr)[NT], int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int row = min(kb + 32 * t + l32, Nk - 1);
+        sr[t] = mfma32<T>(ld128(Kh + (size_t)row * D + 16 * c + 8 * g), qreg[c],
+                          c == 0 ? kZero16 : sr[t]);
+      }
+    apply_mask(sr, kb);
+  };
+
+  auto pv_all = [&](const u32x4 (&pp)[2 * NT], const uint16_t *Vs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 2 * NT; ++k) pv_mfma(Vs, k / 2, k % 2, pp[k]);
+  };
+
+  // One tile kt: s holds its scores (already issued), sn receives those of
+  // tile kt + 1 (from K buffer b ^ 1; past the last tile the result is
+  // unused), pc receives its P. The P V MFMAs of tile kt - 1 (P in pp, V in
+  // V buffer b ^ 1) run in the same step, so that the exponentials of tile
+  // kt overlap both kinds of MFMA.
+  auto step = [&](auto first, int kt, f32x16 (&s)[NT], f32x16 (&sn)[NT], const u32x4 (&pp)[2 * NT],
+                  u32x4 (&pc)[2 * NT], int b) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first)::value;
+    const int kb = kfirst + kt * C::BC;
+    // Every wave's loads of K (kt + 1) and V (kt - 1) have landed, and every
+    // wave is done with K buffer b (read for tile kt) and V buffer b (read
+    // for tile kt - 2), which receive K (kt + 2) and V (kt).
+    wait_vmem_all();
+    __syncthreads();
+    const uint16_t *Kn = kbuf(b ^ 1), *Vp = vbuf(b ^ 1);
+    const i32x4 krs = tile_rsrc(Kh, kt + 2), vrs = tile_rsrc(Vh, kt);
+
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < C::LPW; ++i) dma(krs, gk, kbuf(b), i);
-#pragma unroll
-    for (int c = 1; c < C::NCH; ++c) s_mfma(sn, Kn, c);
-    // Row max of the raw scores (scale > 0 commutes with max).
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[t][r]);
-    mloc = pair_max(mloc);
-    // Reference max: moved only when the row max exceeds it by more than
-    // kMaxSlack (base 2). Any reference gives the same O~ / l; keeping it
-    // bounds P = 2^(s*c2 - m) by 2^kMaxSlack and makes the O~ rescale rare.
-    const float m_cand = fmaxf(m_run, mloc * c2);
-    float alpha = 1.f;
-    if (m_cand > m_run + kMaxSlack) {
-      alpha = fast_exp2(m_run - m_cand);
-      m_run = m_cand;
-    }
-    const float mb = (m_run == -INFINITY) ? 0.f : m_run;  // never form -inf - -inf
-    float psum = 0.f;
-    u32x4 pch[2 * NT];  // chunk 2t + cc
-#pragma unroll
-    for (int k = 0; k < kChunksA; ++k) {
-      pch[k] = p_chunk(s[k / 2], k % 2, mb, psum);
-      // Keep these exponentials in phase A (otherwise they sink past the
-      // rescale branch below).
-      asm volatile("" ::"v"(pch[k]));
-    }
-    asm volatile("" ::"v"(psum));
-    // Issue order: each MFMA with the K read of a later one and a few of the
-    // vector instructions, so the matrix core and the vector ALU overlap;
-    // the direct loads spread out so that no wave waits to issue them.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < kMfmaA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < kMfmaA - 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, kValuA, 0);
-      if (i % kDmaGapA == 0 && i / kDmaGapA < C::LPW)
-        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-    }
+    apply_mask(s, kb);
     __builtin_amdgcn_sched_barrier(0);
-    if (__ballot(alpha != 1.f)) {
+    if constexpr (FIRST) {
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt)
+      for (int i = 0; i < C::LPW; ++i) {
+        dma(krs, gk, kbuf(b), i);
+        dma(vrs, gv, vbuf(b), i);
+      }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      for (int c = 0; c < C::NCH; ++c) s_mfma(sn, Kn, c);
+      float psum;
+      rebase(s, pc, psum);
+      l_run += psum;
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::LPW; ++i) dma(vrs, gv, vbuf(b), i);
+      float psum = 0.f;
+      // Part 1: the P V MFMAs of the previous tile with the first half of
+      // this tile's exponentials.
+      pv_all(pp, Vp);
+#pragma unroll
+      for (int k = 0; k < NT; ++k) pc[k] = p_chunk(s[k / 2], k % 2, m_run, psum);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < kMfmaP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < kMfmaP - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, kValu1, 0);
+        if (i % kDmaGap1 == 0 && i / kDmaGap1 < C::LPW)
+          __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Part 2: the next tile's S MFMAs with the second half.
+#pragma unroll
+      for (int i = 0; i < C::LPW; ++i) dma(krs, gk, kbuf(b), i);
+#pragma unroll
+      for (int c = 0; c < C::NCH; ++c) s_mfma(sn, Kn, c);
+#pragma unroll
+      for (int k = NT; k < 2 * NT; ++k) pc[k] = p_chunk(s[k / 2], k % 2, m_run, psum);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < kMfmaS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < kMfmaS - 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, kValu2, 0);
+        if (i % kDmaGap2 == 0 && i / kDmaGap2 < C::LPW)
+          __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // P > kSumMax somewhere, or a row without a reference yet (m = -inf
+      // makes its P inf or NaN).
+      if (__ballot(!(psum <= kSumMax))) {
+        f32x16 sr[NT];
+        rescore(sr, kb);
+        rebase(sr, pc, psum);
+      }
+      l_run += psum;
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // Phase B: the P V MFMAs, with the second half of the exponentials.
-#pragma unroll
-    for (int k = 0; k < 2 * NT; ++k) {
-      if (k >= kChunksA) pch[k] = p_chunk(s[k / 2], k % 2, mb, psum);
-      pv_mfma(Vs, k / 2, k % 2, pch[k]);
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < C::LPW; ++i) dma(vrs, gv, vbuf(b ^ 1), i);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < kMfmaB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < kMfmaB - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, kValuB, 0);
-      if (i % kDmaGapB == 0 && i / kDmaGapB < C::LPW)
-        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   f32x16 sa[NT], sb[NT];
+  u32x4 pa[2 * NT], pb[2 * NT];
   {
-    const i32x4 k0rs = tile_rsrc(Kh, 0), k1rs = tile_rsrc(Kh, 1), v0rs = tile_rsrc(Vh, 0);
+    const i32x4 k0rs = tile_rsrc(Kh, 0), k1rs = tile_rsrc(Kh, 1);
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       dma(k0rs, gk, K0, i);
-      dma(v0rs, gv, V0, i);
       dma(k1rs, gk, K1, i);
     }
   }
@@ -336,23 +380,32 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
       const int b = kt & 1;
       wait_vmem_all();
       __syncthreads();
-      const i32x4 krs = tile_rsrc(Kh, kt + 2), vrs = tile_rsrc(Vh, kt + 1);
+      const i32x4 krs = tile_rsrc(Kh, kt + 2), vrs = tile_rsrc(Vh, kt);
 #pragma unroll
       for (int i = 0; i < C::LPW; ++i) {
         dma(krs, gk, kbuf(b), i);
-        dma(vrs, gv, vbuf(b ^ 1), i);
+        dma(vrs, gv, vbuf(b), i);
       }
+    }
+    if (ntiles > 0) {
+      wait_vmem_all();
+      __syncthreads();
     }
     return;
   }
+  if (ntiles > 0) {
 #pragma unroll
-  for (int c = 0; c < C::NCH; ++c) s_mfma(sa, kbuf(0), c);
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    step(kt, sa, sb, 0);
-    if (kt + 1 >= ntiles) break;
-    step(kt + 1, sb, sa, 1);
+    for (int c = 0; c < C::NCH; ++c) s_mfma(sa, kbuf(0), c);
+    step(std::true_type{}, 0, sa, sb, pb, pa, 0);
+    // Steps 1 .. ntiles; step ntiles only finishes the P V MFMAs of the
+    // last tile (its own tile lies past the range: fully masked, P = 0).
+    for (int kt = 1;; kt += 2) {
+      step(std::false_type{}, kt, sb, sa, pa, pb, 1);
+      if (kt >= ntiles) break;
+      step(std::false_type{}, kt + 1, sa, sb, pb, pa, 0);
+      if (kt + 1 >= ntiles) break;
+    }
   }
-
   // Epilogue: O = O~ / l, LSE = (m + log2 l) * ln 2.
   const float l_tot = pair_sum(l_run);
   const float inv = fast_rcp(l_tot);

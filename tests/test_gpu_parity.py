@@ -141,6 +141,49 @@ def test_c4_forward_rows_more_slices(fa, oracle_lib):
 
 
 # ---------------------------------------------------------------------------
+# Score ranges that keep moving the running max
+# ---------------------------------------------------------------------------
+
+def _scale_keys(inp, factor):
+    """Key row j multiplied by factor[j], rounded to the dtype again (the
+    oracle sees the same rounded keys)."""
+    dt = inp["k"].dtype
+    inp["k"] = (inp["k"].double() * factor[:, None]).to(dt).contiguous()
+    return inp
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_rising_along_keys(fa, oracle_lib, dt, causal):
+    """Key j scaled by 1 + 40 j / N: a row's largest score keeps growing over
+    the sweep (to about 40 times the usual spread at the end), so the running
+    max m moves in many tiles and O~ and l are rescaled each time."""
+    N = 1000
+    w = ai.custom("rising-%s-%s" % (dt, "c" if causal else "nc"), 1, 2, N, 128, dt, causal,
+                  seed=91)
+    inp = _scale_keys(ai.make_inputs(w, with_do=False),
+                      1 + 40 * torch.arange(N, dtype=torch.float64) / N)
+    got = _run(fa, w, inp, backward=False)
+    _compare_slices(oracle_lib, w, inp, got, [(0, 0), (0, 1)], False)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_key_far_above_the_rest(fa, oracle_lib, dt, causal):
+    """Key 700 scaled by 30: in about half of the rows its score lies tens of
+    units above everything before it, so exponentials taken against the
+    earlier max would overflow fp16 and fp32; the sweep must move m first."""
+    N = 900
+    w = ai.custom("spike-%s-%s" % (dt, "c" if causal else "nc"), 1, 2, N, 64, dt, causal,
+                  seed=92)
+    f = torch.ones(N, dtype=torch.float64)
+    f[700] = 30.0
+    inp = _scale_keys(ai.make_inputs(w, with_do=False), f)
+    got = _run(fa, w, inp, backward=False)
+    _compare_slices(oracle_lib, w, inp, got, [(0, 0), (0, 1)], False)
+
+
+# ---------------------------------------------------------------------------
 # Invariants at full size (no oracle)
 # ---------------------------------------------------------------------------
 
