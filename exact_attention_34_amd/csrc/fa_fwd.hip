@@ -36,9 +36,9 @@
 
 namespace fa {
 
-template <int D>
+template <int D, int W = 4>
 struct FwdCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = W;
   static constexpr int kWavesPerSimd = 2;          // resident waves per SIMD (register budget)
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BR = 32 * kWaves;           // query rows per workgroup, 32 per wave
@@ -94,7 +94,7 @@ __device__ __forceinline__ int swz_v(int row) {
 // normalised) and LSE; PART = true writes the partial result of this key
 // range in fp32 to Op / Lp: O~ / l and m + log l, or 0 and -inf for a row
 // that sees none of these keys.
-template <typename T, int D, bool CAUSAL, bool PART>
+template <typename T, int D, int W, bool CAUSAL, bool PART>
 __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
                                           const uint16_t *__restrict__ K,
                                           const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
@@ -103,7 +103,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
                                           int bh, int qb,
                                           int kfirst, int klim, float c2, uint16_t *K0,
                                           uint16_t *K1, uint16_t *V0, uint16_t *V1) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, W>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int l32 = lane & 31, g = lane >> 5;
@@ -448,12 +448,12 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
 // two workgroup slots of each CU refilled at an even pace (with units of
 // unequal length, freed slots were observed to stay empty for several
 // microseconds), and halves the number of workgroup start-ups.
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void fwd_b16_kernel(
+template <typename T, int D, int W, bool CAUSAL>
+__global__ __launch_bounds__(64 * W, 2) void fwd_b16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int N,
     int nqb, int nunits, int total, float c2) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, W>;
   // Two buffers per tensor, named separately so that the compiler can tell
   // the direct loads into one from the reads of the other.
   __shared__ __attribute__((aligned(1024))) uint16_t K0[C::TILE], K1[C::TILE];
@@ -462,15 +462,15 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void
   const int bh = tile / nunits;
   const int u = tile - bh * nunits;
   if (!CAUSAL) {
-    fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, u, 0, N, c2,
+    fwd_block<T, D, W, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, u, 0, N, c2,
                                    K0, K1, V0, V1);
     return;
   }
-  fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, nqb - 1 - u, 0,
+  fwd_block<T, D, W, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, nqb - 1 - u, 0,
                                  N, c2, K0, K1, V0, V1);
   if (u != nqb - 1 - u) {
     __syncthreads();  // every wave is done with the LDS tiles
-    fwd_block<T, D, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, u, 0, N, c2,
+    fwd_block<T, D, W, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, u, 0, N, c2,
                                    K0, K1, V0, V1);
   }
 }
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void
   const int kfirst = sp * split_keys;
   const int klim = min(Nk, kfirst + split_keys);
   const size_t part = (size_t)sp * BH;
-  fwd_block<T, D, CAUSAL, true>(Q, K, V, nullptr, nullptr, Op + part * Nq * D, Lp + part * Nq,
+  fwd_block<T, D, 4, CAUSAL, true>(Q, K, V, nullptr, nullptr, Op + part * Nq * D, Lp + part * Nq,
                                 Nq, Nk, qoff, bh, qb, kfirst, klim, c2, K0, K1, V0, V1);
 }
 
@@ -682,17 +682,36 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(
   }
 }
 
-template <typename T, int D, bool CAUSAL>
-static hipError_t fwd_b16(int BH, int N, const void *Q, const void *K, const void *V, float c2,
-                          void *O, float *LSE, hipStream_t st) {
-  using C = FwdCfg<D>;
+template <typename T, int D, int W, bool CAUSAL>
+static hipError_t fwd_b16_w(int BH, int N, const void *Q, const void *K, const void *V, float c2,
+                            void *O, float *LSE, hipStream_t st) {
+  using C = FwdCfg<D, W>;
   const int nqb = (N + C::BR - 1) / C::BR;
   const int nunits = CAUSAL ? (nqb + 1) / 2 : nqb;
   const int total = nunits * BH;
-  hipLaunchKernelGGL((fwd_b16_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
+  hipLaunchKernelGGL((fwd_b16_kernel<T, D, W, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
                      (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
                      (uint16_t *)O, LSE, N, nqb, nunits, total, c2);
   return hipGetLastError();
+}
+
+// Workgroup size. Eight waves (256 query rows) share each K and V tile
+// loaded into LDS, half the direct-load traffic of four waves per CU (the
+// loads measured about 13% of the forward's time); four waves (128 rows)
+// when eight-wave units would not give every CU one (few slices or short
+// rows), and under the causal mask for N < 4096, where a 256-row block's
+// masked diagonal tiles cost more than the loads save.
+inline bool fwd_use_w8(int BH, int N, bool causal) {
+  const int nqb = (N + 255) / 256;
+  const long units = (long)BH * (causal ? (nqb + 1) / 2 : nqb);
+  return units >= 256 && (!causal || N >= 4096);
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t fwd_b16(int BH, int N, const void *Q, const void *K, const void *V, float c2,
+                          void *O, float *LSE, hipStream_t st) {
+  return fwd_use_w8(BH, N, CAUSAL) ? fwd_b16_w<T, D, 8, CAUSAL>(BH, N, Q, K, V, c2, O, LSE, st)
+                                   : fwd_b16_w<T, D, 4, CAUSAL>(BH, N, Q, K, V, c2, O, LSE, st);
 }
 
 template <int D, bool CAUSAL>
