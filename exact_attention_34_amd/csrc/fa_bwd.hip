@@ -425,10 +425,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // dQ: query blocks outer, key tiles inner.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int W = 4>
 struct DqCfg {
-  static constexpr int kThreads = 256;             // 4 waves
-  static constexpr int BR = 128;                   // query rows per workgroup, 32 per wave
+  static constexpr int kThreads = 64 * W;          // W waves
+  static constexpr int BR = 32 * W;                // query rows per workgroup, 32 per wave
   static constexpr int BC = 64;                    // keys per tile, two 32-key halves
   static constexpr int CPR = D / 8;
   static constexpr int TILE = BC * D;              // 16-bit elements per K or V tile
@@ -446,13 +446,13 @@ struct DqCfg {
 //
 // One block of query rows (block qb of slice bh). LDS buffer b: K tile at
 // kv + 2*b*TILE, V tile right after it.
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, int W, bool CAUSAL>
 __device__ __forceinline__ void dq_block(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dQ,
     int N, int bh, int qb, float c2, float scale, uint16_t *kv) {
-  using C = DqCfg<D>;
+  using C = DqCfg<D, W>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
@@ -628,25 +628,25 @@ __device__ __forceinline__ void dq_block(
 
 // Work units as in the forward: one query block, or under the causal mask
 // the pair (nqb - 1 - p, p) of blocks with equal total length.
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+template <typename T, int D, int W, bool CAUSAL>
+__global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dQ,
     int N, int nqb, int nunits, int total, float c2, float scale) {
-  using C = DqCfg<D>;
+  using C = DqCfg<D, W>;
   __shared__ __attribute__((aligned(1024))) uint16_t kv[4 * C::TILE];
   const int tile = xcd_tile(blockIdx.x, total);
   const int bh = tile / nunits;
   const int u = tile - bh * nunits;
   if (!CAUSAL) {
-    dq_block<T, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
+    dq_block<T, D, W, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
     return;
   }
-  dq_block<T, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, nqb - 1 - u, c2, scale, kv);
+  dq_block<T, D, W, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, nqb - 1 - u, c2, scale, kv);
   if (u != nqb - 1 - u) {
     __syncthreads();  // every wave is done with the LDS tiles
-    dq_block<T, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
+    dq_block<T, D, W, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
   }
 }
 
@@ -690,16 +690,22 @@ static hipError_t dkdv(const BwdArgs &a, void *dK, void *dV, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL>
-static hipError_t dq(const BwdArgs &a, void *dQ, hipStream_t st) {
-  using C = DqCfg<D>;
+template <typename T, int D, int W, bool CAUSAL>
+static hipError_t dq_w(const BwdArgs &a, void *dQ, hipStream_t st) {
+  using C = DqCfg<D, W>;
   const int nqb = (a.N + C::BR - 1) / C::BR;
   const int nunits = CAUSAL ? (nqb + 1) / 2 : nqb;
   const int total = nunits * a.BH;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st, a.Q,
-                     a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dQ, a.N, nqb, nunits, total,
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, W, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
+                     a.Q, a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dQ, a.N, nqb, nunits, total,
                      a.c2, a.scale);
   return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t dq(const BwdArgs &a, void *dQ, hipStream_t st) {
+  return use_256_row_blocks(a.BH, a.N, CAUSAL) ? dq_w<T, D, 8, CAUSAL>(a, dQ, st)
+                                               : dq_w<T, D, 4, CAUSAL>(a, dQ, st);
 }
 
 static BwdArgs bwd_args(int B, int H, int N, const void *Q, const void *K, const void *V,

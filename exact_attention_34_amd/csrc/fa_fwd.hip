@@ -695,23 +695,12 @@ static hipError_t fwd_b16_w(int BH, int N, const void *Q, const void *K, const v
   return hipGetLastError();
 }
 
-// Workgroup size. Eight waves (256 query rows) share each K and V tile
-// loaded into LDS, half the direct-load traffic of four waves per CU (the
-// loads measured about 13% of the forward's time); four waves (128 rows)
-// when eight-wave units would not give every CU one (few slices or short
-// rows), and under the causal mask for N < 4096, where a 256-row block's
-// masked diagonal tiles cost more than the loads save.
-inline bool fwd_use_w8(int BH, int N, bool causal) {
-  const int nqb = (N + 255) / 256;
-  const long units = (long)BH * (causal ? (nqb + 1) / 2 : nqb);
-  return units >= 256 && (!causal || N >= 4096);
-}
-
 template <typename T, int D, bool CAUSAL>
 static hipError_t fwd_b16(int BH, int N, const void *Q, const void *K, const void *V, float c2,
                           void *O, float *LSE, hipStream_t st) {
-  return fwd_use_w8(BH, N, CAUSAL) ? fwd_b16_w<T, D, 8, CAUSAL>(BH, N, Q, K, V, c2, O, LSE, st)
-                                   : fwd_b16_w<T, D, 4, CAUSAL>(BH, N, Q, K, V, c2, O, LSE, st);
+  return use_256_row_blocks(BH, N, CAUSAL)
+             ? fwd_b16_w<T, D, 8, CAUSAL>(BH, N, Q, K, V, c2, O, LSE, st)
+             : fwd_b16_w<T, D, 4, CAUSAL>(BH, N, Q, K, V, c2, O, LSE, st);
 }
 
 template <int D, bool CAUSAL>

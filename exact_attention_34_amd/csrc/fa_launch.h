@@ -12,6 +12,19 @@ hipError_t launch_fwd(int dtype, int B, int H, int N, int d, const void *Q, cons
                       const void *V, float scale, int causal, void *O, float *LSE,
                       hipStream_t stream);
 
+// Workgroup size of the query-block-outer sweeps (forward, dQ). Eight waves
+// (256 query rows) share each K and V tile loaded into LDS, half the
+// direct-load traffic of four waves per CU (the loads measured about 13% of
+// the forward's time); four waves (128 rows) when eight-wave units would not
+// give every CU one (few slices or short rows), and under the causal mask
+// for N < 4096, where a 256-row block runs more fully masked diagonal tiles
+// than the loads save.
+inline bool use_256_row_blocks(int BH, int N, bool causal) {
+  const int nqb = (N + 255) / 256;
+  const long units = (long)BH * (causal ? (nqb + 1) / 2 : nqb);
+  return units >= 256 && (!causal || N >= 4096);
+}
+
 // Split-key forward: key tiles (64 keys) are divided into ranges of
 // split_key_count(N, nsplit) keys, split_parts(N, nsplit) <= nsplit of them,
 // none empty.

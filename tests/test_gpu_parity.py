@@ -142,14 +142,14 @@ def test_c4_forward_rows_more_slices(fa, oracle_lib):
 
 @pytest.mark.parametrize("causal,N", [(False, 4000), (True, 4500)])
 def test_eight_wave_blocks_ragged(fa, oracle_lib, causal, N):
-    """Shapes on which the forward runs 256-row workgroups (B*H = 64 slices
-    give at least one such unit per CU, and N >= 4096 under the mask), with
-    a partial last block and a partial last key tile."""
+    """Shapes on which the forward and the dQ sweep run 256-row workgroups
+    (B*H = 64 slices give at least one such unit per CU, and N >= 4096 under
+    the mask), with a partial last block and a partial last key tile."""
     w = ai.custom("w8-%s-N%d" % ("c" if causal else "nc", N), 4, 16, N, 128, "bf16", causal,
                   seed=55)
-    inp = ai.make_inputs(w, with_do=False)
-    got = _run(fa, w, inp, backward=False)
-    _compare_slices(oracle_lib, w, inp, got, [(0, 0), (3, 15)], False)
+    inp = ai.make_inputs(w)
+    got = _run(fa, w, inp)
+    _compare_slices(oracle_lib, w, inp, got, [(0, 0), (3, 15)], True)
 
 
 # ---------------------------------------------------------------------------
