@@ -76,6 +76,15 @@ def lib():
     L.fa_bwd_dkdv.restype = i
     L.fa_bwd_dq.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p]
     L.fa_bwd_dq.restype = i
+    L.fa_std_row_stride.argtypes = [i]
+    L.fa_std_row_stride.restype = i
+    for name in ("fa_std_p_bytes", "fa_std_fwd_workspace_bytes", "fa_std_bwd_workspace_bytes"):
+        getattr(L, name).argtypes = [i, i, i, i, i]
+        getattr(L, name).restype = z
+    L.fa_std_fwd.argtypes = [i, i, i, i, i, p, p, p, f, i, p, p, p, p, z, p]
+    L.fa_std_fwd.restype = i
+    L.fa_std_bwd.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, p, p, p, p, z, p]
+    L.fa_std_bwd.restype = i
     _lib = L
     return L
 
@@ -235,3 +244,51 @@ def bwd_dq(q, k, v, do, lse, dvec, dq, scale=None, causal=False):
     dt, B, H, N, d = _check_qkv(q, k, v, do, dq)
     _call("fa_bwd_dq", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
           _ptr(dvec), _scale(scale, d), int(bool(causal)), _ptr(dq), _stream(q))
+
+
+def std_row_stride(N):
+    """Row stride (elements) of the N x N arrays of the standard path."""
+    return int(lib().fa_std_row_stride(N))
+
+
+def std_p_bytes(dtype, B, H, N, d):
+    return int(lib().fa_std_p_bytes(_CODES[dtype], B, H, N, d))
+
+
+def std_fwd_workspace_bytes(dtype, B, H, N, d):
+    return int(lib().fa_std_fwd_workspace_bytes(_CODES[dtype], B, H, N, d))
+
+
+def std_bwd_workspace_bytes(dtype, B, H, N, d):
+    return int(lib().fa_std_bwd_workspace_bytes(_CODES[dtype], B, H, N, d))
+
+
+def std_fwd(q, k, v, scale=None, causal=False, workspace=None):
+    """O, LSE, P of standard attention that stores S and P in device memory.
+    P is [B, H, N, std_row_stride(N)] in q's dtype (padding columns zero)."""
+    dt, B, H, N, d = _check_qkv(q, k, v)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    P = torch.empty((B, H, N, std_row_stride(N)), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(std_fwd_workspace_bytes(q.dtype, B, H, N, d), dtype=torch.uint8,
+                                device=q.device)
+    _call("fa_std_fwd", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _scale(scale, d),
+          int(bool(causal)), _ptr(o), _ptr(lse), _ptr(P), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(q))
+    return o, lse, P
+
+
+def std_bwd(q, k, v, o, do, P, scale=None, workspace=None):
+    """dQ, dK, dV of the standard path from the stored P of std_fwd()."""
+    dt, B, H, N, d = _check_qkv(q, k, v, o, do)
+    if P.shape != (B, H, N, std_row_stride(N)) or P.dtype != q.dtype or not P.is_contiguous():
+        raise ValueError("P must be std_fwd's [B, H, N, row stride] array")
+    if workspace is None:
+        workspace = torch.empty(std_bwd_workspace_bytes(q.dtype, B, H, N, d), dtype=torch.uint8,
+                                device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _call("fa_std_bwd", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(P),
+          _scale(scale, d), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(q))
+    return dq, dk, dv

@@ -106,6 +106,18 @@ int run_split(int dtype, int B, int H, int Nq, int Nk, int d, const void *Q, con
   return status(fa::launch_lse_merge(dtype, parts, (long)B * H * Nq, d, Op, Lp, O, LSE, st));
 }
 
+// Standard attention: N x N element count per call, or 0 when too large.
+size_t std_elems(int B, int H, int N) {
+  const size_t e = (size_t)B * H * N * fa::std_row_stride(N);
+  return e < (1ULL << 38) ? e : 0;
+}
+int check_std(int dtype, int B, int H, int N, int d) {
+  const int rc = check_shape(dtype, B, H, N, d, true);
+  if (rc != FA_OK) return rc;
+  return std_elems(B, H, N) ? FA_OK : FA_ERR_INVALID_ARG;
+}
+size_t std_ds_bytes(int B, int H, int N) { return round_up(std_elems(B, H, N) * 2, kWsAlign); }
+
 }  // namespace
 
 extern "C" {
@@ -265,6 +277,53 @@ int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, 
     return rc;
   return status(
       fa::launch_bwd_dq(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal, dQ, st));
+}
+
+int fa_std_row_stride(int N) { return N > 0 ? fa::std_row_stride(N) : 0; }
+
+size_t fa_std_p_bytes(int dtype, int B, int H, int N, int d) {
+  if (check_std(dtype, B, H, N, d) != FA_OK) return 0;
+  return std_elems(B, H, N) * 2;
+}
+
+size_t fa_std_fwd_workspace_bytes(int dtype, int B, int H, int N, int d) {
+  if (check_std(dtype, B, H, N, d) != FA_OK) return 0;
+  return round_up(std_elems(B, H, N) * sizeof(float), kWsAlign);
+}
+
+size_t fa_std_bwd_workspace_bytes(int dtype, int B, int H, int N, int d) {
+  if (check_std(dtype, B, H, N, d) != FA_OK) return 0;
+  return std_ds_bytes(B, H, N) + d_bytes(B, H, N);
+}
+
+int fa_std_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
+               float scale, int causal, void *O, float *LSE, void *P, void *workspace,
+               size_t workspace_bytes, void *stream) {
+  int rc = check_std(dtype, B, H, N, d);
+  if (rc != FA_OK) return rc;
+  if ((rc = check_scale_causal(scale, causal)) != FA_OK) return rc;
+  if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O) || !vec_ok(LSE) ||
+      !tensor_ok(P) || workspace == nullptr || !aligned(workspace, kWsAlign))
+    return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_std_fwd_workspace_bytes(dtype, B, H, N, d)) return FA_ERR_WORKSPACE;
+  return status(fa::launch_std_fwd(dtype, B, H, N, d, Q, K, V, scale, causal, (float *)workspace,
+                                   P, O, LSE, (hipStream_t)stream));
+}
+
+int fa_std_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
+               const void *O, const void *dO, const void *P, float scale, void *dQ, void *dK,
+               void *dV, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_std(dtype, B, H, N, d);
+  if (rc != FA_OK) return rc;
+  if ((rc = check_scale_causal(scale, 0)) != FA_OK) return rc;
+  if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O) || !tensor_ok(dO) ||
+      !tensor_ok(P) || !tensor_ok(dQ) || !tensor_ok(dK) || !tensor_ok(dV) ||
+      workspace == nullptr || !aligned(workspace, kWsAlign))
+    return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_std_bwd_workspace_bytes(dtype, B, H, N, d)) return FA_ERR_WORKSPACE;
+  float *Dv = (float *)((char *)workspace + std_ds_bytes(B, H, N));
+  return status(fa::launch_std_bwd(dtype, B, H, N, d, Q, K, V, O, dO, P, scale, workspace, Dv,
+                                   dQ, dK, dV, (hipStream_t)stream));
 }
 
 }  // extern "C"

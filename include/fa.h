@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 /* element types */
 #define FA_F32 0
@@ -233,6 +233,59 @@ int fa_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q,
               const void *K, const void *V, const void *dO, const float *LSE,
               const float *Dvec, float scale, int causal, void *dQ,
               void *stream);
+
+/*
+ * Standard attention that stores the N x N matrices: the method the pages
+ * set tiled attention against ([FA] section 1: S = Q K^T and P = softmax(S)
+ * written out whole before O = P V; section 3: the backward that reads the
+ * stored P instead of recomputing it). It exists to measure that trade-off
+ * on this chip (time and device memory against fa_fwd / fa_bwd); it gives
+ * the same results within rounding. Every step is a separate kernel and
+ * every N x N intermediate goes through device memory:
+ *   forward:  S = scale Q K^T (fp32, -inf where masked), P = softmax(S)
+ *             rounded to dtype, O = P V, LSE = log sum_j exp(S_ij);
+ *   backward: D = rowsum(dO o O), dV = P^T dO, dS = P o (dO V^T - D)
+ *             rounded to dtype, dQ = scale dS K, dK = scale dS^T Q.
+ * N x N arrays of a slice are row-major with fa_std_row_stride(N) elements
+ * per row (N rounded up to a multiple of 128); the padding columns of P
+ * hold zeros. dtype: FA_F16 and FA_BF16 (FA_F32 returns
+ * FA_ERR_UNSUPPORTED). Size limit: B*H*N*fa_std_row_stride(N) < 2^38.
+ */
+int fa_std_row_stride(int N);
+
+/* Bytes of P: dtype [B, H, N, fa_std_row_stride(N)]; 0 if invalid. */
+size_t fa_std_p_bytes(int dtype, int B, int H, int N, int d);
+
+/* Forward workspace: S fp32 [B, H, N, row stride]; 0 if invalid. */
+size_t fa_std_fwd_workspace_bytes(int dtype, int B, int H, int N, int d);
+
+/* Backward workspace: dS dtype [B, H, N, row stride], then D fp32
+ * [B, H, N] (each part rounded up to 256 bytes); 0 if invalid. */
+size_t fa_std_bwd_workspace_bytes(int dtype, int B, int H, int N, int d);
+
+/*
+ * In:  Q, K, V [B, H, N, d] dtype.
+ * Out: O [B, H, N, d] dtype; LSE [B, H, N] fp32; P (at least
+ *      fa_std_p_bytes bytes), kept by the caller for fa_std_bwd.
+ * workspace: at least fa_std_fwd_workspace_bytes bytes, 256-byte aligned;
+ *   overwritten.
+ */
+int fa_std_fwd(int dtype, int B, int H, int N, int d, const void *Q,
+               const void *K, const void *V, float scale, int causal, void *O,
+               float *LSE, void *P, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/*
+ * In:  Q, K, V, O, dO [B, H, N, d] dtype; P as fa_std_fwd wrote it for the
+ *      same inputs (it carries the causal mask as zeros).
+ * Out: dQ, dK, dV [B, H, N, d] dtype.
+ * workspace: at least fa_std_bwd_workspace_bytes bytes, 256-byte aligned;
+ *   overwritten.
+ */
+int fa_std_bwd(int dtype, int B, int H, int N, int d, const void *Q,
+               const void *K, const void *V, const void *O, const void *dO,
+               const void *P, float scale, void *dQ, void *dK, void *dV,
+               void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -204,3 +204,59 @@ def test_kvcache_parts_and_workspace(L, Nq, Nk, nsplit, parts):
     ob = -(-parts * 6 * Nq * 128 * 4 // 256) * 256
     lb = -(-parts * 6 * Nq * 4 // 256) * 256
     assert L.fa_fwd_kvcache_workspace_bytes(2, 2, 3, Nq, Nk, 128, nsplit) == ob + lb
+
+
+# ---------------------------------------------------------------------------
+# Standard attention (stores S and P)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,ld", [(1, 128), (128, 128), (129, 256), (1000, 1024), (2048, 2048)])
+def test_std_row_stride_and_bytes(L, N, ld):
+    """N x N arrays have rows of N rounded up to 128 elements; P is 16-bit, S
+    fp32, the backward workspace dS (16-bit) then D (fp32), each part padded
+    to 256 bytes."""
+    r = lambda x: -(-x // 256) * 256
+    assert L.fa_std_row_stride(N) == ld
+    B, H, d = 2, 3, 64
+    assert L.fa_std_p_bytes(2, B, H, N, d) == B * H * N * ld * 2
+    assert L.fa_std_fwd_workspace_bytes(1, B, H, N, d) == r(B * H * N * ld * 4)
+    assert L.fa_std_bwd_workspace_bytes(2, B, H, N, d) == r(B * H * N * ld * 2) + r(B * H * N * 4)
+    assert L.fa_std_p_bytes(0, B, H, N, d) == 0            # fp32 is not built
+    assert L.fa_std_fwd_workspace_bytes(2, B, H, N, 96) == 0
+    assert L.fa_std_bwd_workspace_bytes(2, 0, H, N, d) == 0
+
+
+def _std_fwd(L, dtype=2, N=16, d=64, scale=0.125, causal=0, o=A2, P=A2, ws=A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = L.fa_std_fwd_workspace_bytes(dtype, 1, 1, N, d)
+    return L.fa_std_fwd(dtype, 1, 1, N, d, A, A, A, scale, causal, o, A2, P, ws, ws_bytes,
+                        None)
+
+
+def _std_bwd(L, dtype=2, N=16, d=64, scale=0.125, P=A, dq=A2, ws=A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = L.fa_std_bwd_workspace_bytes(dtype, 1, 1, N, d)
+    return L.fa_std_bwd(dtype, 1, 1, N, d, A, A, A, A, A, P, scale, dq, A2, A2, ws, ws_bytes,
+                        None)
+
+
+def test_std_rejects(L):
+    assert _std_fwd(L, dtype=0) == UNSUP
+    assert _std_fwd(L, d=32) == UNSUP
+    assert _std_fwd(L, N=0) == INVALID
+    assert _std_fwd(L, scale=math.inf) == INVALID
+    assert _std_fwd(L, causal=2) == INVALID
+    assert _std_fwd(L, o=MIS) == INVALID
+    assert _std_fwd(L, P=NUL) == INVALID
+    assert _std_fwd(L, ws=ctypes.c_void_p(0x10010)) == INVALID   # workspace not 256-aligned
+    assert _std_fwd(L, ws_bytes=L.fa_std_fwd_workspace_bytes(2, 1, 1, 16, 64) - 1) == WS
+    # B*H*N*d < 2^31, but 64 slices of 65536 x 65536 reach the 2^38 limit
+    assert L.fa_std_fwd(2, 8, 8, 1 << 16, 64, A, A, A, 0.1, 0, A2, A2, A2, A, 1 << 62,
+                        None) == INVALID
+    assert L.fa_std_p_bytes(2, 8, 8, 1 << 16, 64) == 0
+    assert _std_bwd(L, dtype=0) == UNSUP
+    assert _std_bwd(L, scale=0.0) == INVALID
+    assert _std_bwd(L, P=MIS) == INVALID
+    assert _std_bwd(L, dq=NUL) == INVALID
+    assert _std_bwd(L, ws=NUL) == INVALID
+    assert _std_bwd(L, ws_bytes=L.fa_std_bwd_workspace_bytes(2, 1, 1, 16, 64) - 1) == WS
