@@ -303,6 +303,79 @@ def kvcache_report(fa, torch, settle_s):
     return out
 
 
+def std_report(fa, torch, settle_s):
+    """Standard attention that stores S and P (the pages' baseline) against
+    the tiled path on the same inputs: time and the device memory of the
+    N x N arrays (S fp32 and P in the forward, dS in the backward) against
+    the tiled path's only per-row extras (LSE and D, fp32)."""
+    import attn_inputs as ai
+    L = fa.lib()
+    out = []
+    for w in (ai.WORKLOADS["c5"], ai.WORKLOADS["perf-2k"], ai.WORKLOADS["perf-8k"]):
+        d = {k: v.cuda() for k, v in ai.make_inputs(w).items()}
+        B, H, N, D = w.B, w.H, w.N, w.d
+        dt = d["q"].dtype
+        code = {torch.bfloat16: fa.BF16, torch.float16: fa.F16}[dt]
+        P_ = lambda t: t.data_ptr()
+        st = torch.cuda.current_stream().cuda_stream
+        o, lse = torch.empty_like(d["q"]), torch.empty((B, H, N), dtype=torch.float32,
+                                                       device="cuda")
+        dq, dk, dv = (torch.empty_like(d["q"]) for _ in range(3))
+        pbytes = fa.std_p_bytes(dt, B, H, N, D)
+        fws = fa.std_fwd_workspace_bytes(dt, B, H, N, D)
+        bws = fa.std_bwd_workspace_bytes(dt, B, H, N, D)
+        Pm = torch.empty(pbytes, dtype=torch.uint8, device="cuda")
+        ws = torch.empty(max(fws, bws), dtype=torch.uint8, device="cuda")
+        gws = torch.empty(fa.bwd_workspace_bytes(dt, B, H, N, D), dtype=torch.uint8,
+                          device="cuda")
+
+        def ck(rc):
+            if rc != 0:
+                raise RuntimeError("library call failed: %d" % rc)
+
+        def std_f():
+            ck(L.fa_std_fwd(code, B, H, N, D, P_(d["q"]), P_(d["k"]), P_(d["v"]), w.scale,
+                            int(w.causal), P_(o), P_(lse), P_(Pm), P_(ws), fws, st))
+
+        def std_fb():
+            std_f()
+            ck(L.fa_std_bwd(code, B, H, N, D, P_(d["q"]), P_(d["k"]), P_(d["v"]), P_(o),
+                            P_(d["do"]), P_(Pm), w.scale, P_(dq), P_(dk), P_(dv), P_(ws), bws,
+                            st))
+
+        def fl_f():
+            ck(L.fa_fwd(code, B, H, N, D, P_(d["q"]), P_(d["k"]), P_(d["v"]), w.scale,
+                        int(w.causal), P_(o), P_(lse), st))
+
+        def fl_fb():
+            fl_f()
+            ck(L.fa_bwd(code, B, H, N, D, P_(d["q"]), P_(d["k"]), P_(d["v"]), P_(o),
+                        P_(d["do"]), P_(lse), w.scale, int(w.causal), P_(dq), P_(dk), P_(dv),
+                        P_(gws), gws.numel(), st))
+
+        ms = {name: _time_ms(torch, fn, 5, settle_s)
+              for name, fn in (("std_fwd", std_f), ("std_fwdbwd", std_fb), ("fwd", fl_f),
+                               ("fwdbwd", fl_fb))}
+        flops = w.fwd_flops(), w.fwd_flops() + w.bwd_flops()
+        nxn = fws + pbytes + bws - fa.bwd_workspace_bytes(dt, B, H, N, D)
+        rec = {"workload": w.name, "B": B, "H": H, "N": N, "d": D, "causal": w.causal,
+               "std_fwd_ms": round(ms["std_fwd"], 3), "std_fwdbwd_ms": round(ms["std_fwdbwd"], 3),
+               "fwd_ms": round(ms["fwd"], 3), "fwdbwd_ms": round(ms["fwdbwd"], 3),
+               "std_fwd_tflops": round(flops[0] / ms["std_fwd"] / 1e9, 1),
+               "std_fwdbwd_tflops": round(flops[1] / ms["std_fwdbwd"] / 1e9, 1),
+               "fwd_speedup": round(ms["std_fwd"] / ms["fwd"], 2),
+               "fwdbwd_speedup": round(ms["std_fwdbwd"] / ms["fwdbwd"], 2),
+               "nxn_gib": round(nxn / 2 ** 30, 2),
+               "tiled_extra_mib": round(2 * B * H * N * 4 / 2 ** 20, 2)}
+        out.append(rec)
+        print("# std %s: stored-P fwd %.3f ms, fwd+bwd %.3f ms; tiled %.3f / %.3f ms; N x N "
+              "arrays %.2f GiB" % (w.name, ms["std_fwd"], ms["std_fwdbwd"], ms["fwd"],
+                                   ms["fwdbwd"], nxn / 2 ** 30), file=sys.stderr, flush=True)
+        del Pm, ws, gws, d
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +388,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-splitkv", action="store_true")
     ap.add_argument("--no-kvcache", action="store_true")
+    ap.add_argument("--no-std", action="store_true",
+                    help="skip the stored-P standard-attention comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales the HBM "
                          "byte counters read under rocprofv3)")
@@ -402,6 +477,8 @@ def main():
         out["splitkv"] = splitkv_report(fa, torch, min(args.settle, 0.5))
     if not args.no_kvcache:
         out["kvcache"] = kvcache_report(fa, torch, min(args.settle, 0.5))
+    if not args.no_std:
+        out["standard"] = std_report(fa, torch, min(args.settle, 0.5))
     print(json.dumps(out), flush=True)
 
 

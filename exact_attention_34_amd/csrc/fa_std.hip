@@ -153,6 +153,24 @@ __global__ __launch_bounds__(256, 2) void std_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < C::WN; ++j) acc[i][j] = kZero16;
 
+  // The dS epilogue's P values, loaded before the (short, K = d) product so
+  // that their latency overlaps it: the same (row, 4-column run) positions
+  // the epilogue below writes.
+  u32x2 pre[2][C::WN][4];
+  if constexpr (EPI == kEpiDs) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = min(m0 + 64 * wm + 32 * i + l32, M - 1);
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + (NC / 2) * wn + 32 * j + 8 * q + 4 * g;
+          pre[i][j][q] = *(const u32x2 *)(P + z * sC + (size_t)row * ldpv + col);
+        }
+    }
+  }
+
   const int nk = Kend / C::BK;
   load(0);
   stash(0);
@@ -172,53 +190,86 @@ __global__ __launch_bounds__(256, 2) void std_gemm_kernel(
       for (int j = 0; j < C::WN; ++j)
         b[j] = TB == 1 ? opnd_row(Bb, (NC / 2) * wn + 32 * j, kk)
                        : opnd_col(Bb, C::SC_B, (NC / 2) * wn + 32 * j, kk);
+      // The fp32 scores: A as the first operand, so that the result's lane
+      // is a column of C (32 lanes store 128 contiguous bytes of a row).
+      // The 16-bit outputs: B first, so that the lane is a row of C and
+      // its registers are columns (each lane stores runs of 4 columns).
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < C::WN; ++j) acc[i][j] = mfma32<T>(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < C::WN; ++j)
+          acc[i][j] = EPI == kEpiScores ? mfma32<T>(a[i], b[j], acc[i][j])
+                                        : mfma32<T>(b[j], a[i], acc[i][j]);
     }
     if (kt + 1 < nk) stash(buf ^ 1);
     __syncthreads();
   }
 
-  // Result block (i, j): lane holds column n = l%32 and rows 8(r/4) + 4g +
-  // r%4 of its 32 x 32 block.
+  if constexpr (EPI == kEpiScores) {
+    // Result block (i, j): lane holds column l%32 of its 32 x 32 block and
+    // rows 8(r/4) + 4g + r%4 in register r.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < C::WN; ++j) {
-      const int col = n0 + (NC / 2) * wn + 32 * j + l32;
+      for (int j = 0; j < C::WN; ++j) {
+        const int col = n0 + (NC / 2) * wn + 32 * j + l32;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = m0 + 64 * wm + 32 * i + 8 * (rr >> 2) + 4 * g + (rr & 3);
-        if (row >= M) continue;
-        const float x = acc[i][j][rr];
-        const size_t at = z * sC + (size_t)row * ldc + col;
-        if constexpr (EPI == kEpiScores) {
+        for (int rr = 0; rr < 16; ++rr) {
+          const int row = m0 + 64 * wm + 32 * i + 8 * (rr >> 2) + 4 * g + (rr & 3);
+          if (row >= M) continue;
           const bool masked = col >= ncols_valid || (causal && col > row);
-          ((float *)Cout)[at] = masked ? -INFINITY : x * scale;
-        } else if constexpr (EPI == kEpiStore) {
-          const uint32_t h = pack2<T>(x * scale, 0.f);
-          ((uint16_t *)Cout)[at] = (uint16_t)(h & 0xffffu);
-        } else {
-          const size_t pat = z * sC + (size_t)row * ldpv + col;
-          const float p = to_f32<T>(P[pat]);
-          const float ds = col < ncols_valid ? p * (x - Dv[(size_t)z * M + row]) : 0.f;
-          const uint32_t h = pack2<T>(ds, 0.f);
-          ((uint16_t *)Cout)[at] = (uint16_t)(h & 0xffffu);
+          ((float *)Cout)[z * sC + (size_t)row * ldc + col] =
+              masked ? -INFINITY : acc[i][j][rr] * scale;
         }
       }
-    }
+    return;
+  }
+  // Result block (i, j): lane holds row m = l%32 of its 32 x 32 block and
+  // columns 8q + 4g + (0..3) in registers 4q .. 4q+3.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = m0 + 64 * wm + 32 * i + l32;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + (NC / 2) * wn + 32 * j + 8 * q + 4 * g;
+        const size_t at = z * sC + (size_t)row * ldc + col;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[i][j][4 * q + e];
+        if constexpr (EPI == kEpiDs) {
+          const u32x2 pv = pre[i][j][q];
+          const float dd = Dv[(size_t)z * M + row];
+          const float p[4] = {to_f32<T>((uint16_t)(pv[0] & 0xffffu)),
+                              to_f32<T>((uint16_t)(pv[0] >> 16)),
+                              to_f32<T>((uint16_t)(pv[1] & 0xffffu)),
+                              to_f32<T>((uint16_t)(pv[1] >> 16))};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = col + e < ncols_valid ? p[e] * (x[e] - dd) : 0.f;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] *= scale;
+        }
+        u32x2 o;
+        o[0] = pack2<T>(x[0], x[1]);
+        o[1] = pack2<T>(x[2], x[3]);
+        *(u32x2 *)((uint16_t *)Cout + at) = o;
+      }
+  }
 }
 
 // One row of S (fp32, ldn columns of which the first N exist): P = exp(S -
-// m) / l rounded to T (0 in the padding columns), LSE = m + log l. Three
-// passes over the row: max, sum, write.
+// m) / l rounded to T (0 in the padding columns), LSE = m + log l. The row
+// is read from device memory once and kept in registers (4 * kCache
+// values per thread, rows up to 8192); longer rows re-read the rest.
 template <typename T>
 __global__ __launch_bounds__(256) void std_softmax_kernel(const float *__restrict__ S,
                                                           uint16_t *__restrict__ P,
                                                           float *__restrict__ LSE, int N,
                                                           int ldn) {
+  constexpr int kCache = 8;
   __shared__ float red[4];
   const long row = blockIdx.x;  // slice-major: row = z * N + i
   const float *s = S + row * ldn;
@@ -236,33 +287,55 @@ __global__ __launch_bounds__(256) void std_softmax_kernel(const float *__restric
     const float a = red[0], b = red[1], c = red[2], d = red[3];
     return is_max ? fmaxf(fmaxf(a, b), fmaxf(c, d)) : (a + b) + (c + d);
   };
-  float m = -INFINITY;
-  for (int j = 4 * tid; j < N; j += 1024) {
-    const f32x4 v = *(const f32x4 *)(s + j);
+  // Chunk c of this thread: columns 4 tid + 1024 c .. +3 (ldn is a multiple
+  // of 128, so a chunk is inside the row or wholly past it).
+  f32x4 v[kCache];
+  auto chunk = [&](int c) __attribute__((always_inline)) {
+    const int j = 4 * tid + 1024 * c;
+    f32x4 x = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (j < ldn) x = *(const f32x4 *)(s + j);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (j + e < N) m = fmaxf(m, v[e]);
+      if (j + e >= N) x[e] = -INFINITY;
+    return x;
+  };
+  const int nch = (ldn + 1023) / 1024;
+#pragma unroll
+  for (int c = 0; c < kCache; ++c) v[c] = c < nch ? chunk(c) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float m = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kCache; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, v[c][e]);
+  for (int c = kCache; c < nch; ++c) {
+    const f32x4 x = chunk(c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, x[e]);
   }
   m = block_reduce(m, true);
   float l = 0.f;
-  for (int j = 4 * tid; j < N; j += 1024) {
-    const f32x4 v = *(const f32x4 *)(s + j);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (j + e < N) l += __expf(v[e] - m);
+  for (int c = 0; c < kCache; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) l += __expf(v[c][e] - m);
+  for (int c = kCache; c < nch; ++c) {
+    const f32x4 x = chunk(c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) l += __expf(x[e] - m);
   }
   l = block_reduce(l, false);
   const float inv = 1.f / l;
-  for (int j = 4 * tid; j < ldn; j += 1024) {
-    const f32x4 v = *(const f32x4 *)(s + j);
-    float q[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) q[e] = j + e < N ? __expf(v[e] - m) * inv : 0.f;
+  auto put = [&](int c, const f32x4 &x) __attribute__((always_inline)) {
+    const int j = 4 * tid + 1024 * c;
+    if (j >= ldn) return;
     u32x2 o;
-    o[0] = pack2<T>(q[0], q[1]);
-    o[1] = pack2<T>(q[2], q[3]);
+    o[0] = pack2<T>(__expf(x[0] - m) * inv, __expf(x[1] - m) * inv);
+    o[1] = pack2<T>(__expf(x[2] - m) * inv, __expf(x[3] - m) * inv);
     *(u32x2 *)(p + j) = o;
-  }
+  };
+#pragma unroll
+  for (int c = 0; c < kCache; ++c) put(c, v[c]);
+  for (int c = kCache; c < nch; ++c) put(c, chunk(c));
   if (tid == 0) LSE[row] = m + __logf(l);
 }
 
