@@ -7,6 +7,7 @@
 
 #include "fa.h"
 #include "fa_launch.h"
+#include "fa_std_launch.h"
 
 namespace {
 

@@ -25,6 +25,7 @@
 
 #include "fa_device.h"
 #include "fa_launch.h"
+#include "fa_std_launch.h"
 
 namespace fa {
 
