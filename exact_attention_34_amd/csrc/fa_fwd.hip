@@ -217,7 +217,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
   // direct load every kDmaGap MFMAs (V loads in the first part, K in the
   // second).
   constexpr int kMfmaS = NT * C::NCH, kMfmaP = 2 * NT * C::NDT;
-  constexpr int kValu1 = (D == 128) ? 3 : 8, kValu2 = (D == 128) ? 4 : 8;
+  constexpr int kValu1 = (D == 128) ? 3 : 6, kValu2 = (D == 128) ? 3 : 6;
   constexpr int kDmaGap1 = kMfmaP / C::LPW, kDmaGap2 = kMfmaS / C::LPW;
   // Bound on each lane's sum of P against the current reference (below the
   // fp16 maximum, 65504).
