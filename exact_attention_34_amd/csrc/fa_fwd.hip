@@ -1,13 +1,14 @@
 // fa_fwd.hip -- forward pass of exact attention on gfx950.
 //
-// One workgroup computes BR query rows of one (batch, head) slice and sweeps
-// the key/value tiles once ("Flash Attention" notes, section 1: Q blocks in
-// the outer loop, K/V blocks in the inner one; section 2, part 4.2: the
-// forward loop). Per tile it keeps the running row max m and normaliser l and
-// rescales the unnormalised output O~ by exp(m_old - m_new) (section 2,
-// parts 3.1 and 4.1, the two-block merges), so no N x N array is formed; the
-// division by l is deferred to the end and LSE = m + log l is returned for
-// the backward (section 3, part 3).
+// One workgroup (4 or 8 waves) computes BR = 32 * waves query rows of one
+// (batch, head) slice and sweeps the key/value tiles once ("Flash Attention"
+// notes, section 1: Q blocks in the outer loop, K/V blocks in the inner one;
+// section 2, part 4.2: the forward loop). It keeps a running reference m and
+// normaliser l per row and rescales the unnormalised output O~ by
+// exp(m_old - m_new) whenever m moves (section 2, parts 3.1 and 4.1, the
+// two-block merges), so no N x N array is formed; the division by l is
+// deferred to the end and LSE = m + log l is returned for the backward
+// (section 3, part 3).
 //
 // Work is done in base 2: scores are scaled by scale * log2(e) so that one
 // v_exp_f32 (2^x) gives each exponential, and m is kept in those units.
@@ -24,8 +25,9 @@
 //     tile with transposing LDS reads (ds_read_b64_tr_b16).
 //   * K and V tiles are double-buffered in LDS (row-major, XOR-swizzled at
 //     16-byte granularity) and filled by direct buffer->LDS loads
-//     (buffer_load_dwordx4 ... lds): the loads of tile j+1 are issued right
-//     after the barrier that opens tile j and land while tile j is computed.
+//     (buffer_load_dwordx4 ... lds), issued between the MFMAs of the step
+//     that opens with the barrier: K two tiles ahead, V one step before it is
+//     used. The waves of a workgroup share every tile.
 // The fp32 variant is the same loop on v_mfma_f32_32x32x2_f32 with P kept in
 // fp32.
 
