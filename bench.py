@@ -96,18 +96,17 @@ def _step_fns(fa, torch, w, d):
         ck(L.fa_fwd(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), w.scale, c, P(o),
                     P(lse), st))
 
-    def pre():
-        ck(L.fa_bwd_preprocess(code, B, H, N, D, P(o), P(d["do"]), P(dvec), st))
+    # fa_bwd's own sequence, one ABI call per sweep so that each can be timed:
+    # the dQ sweep (which also forms D = rowsum(dO o O)), then dK/dV.
+    def dqs():
+        ck(L.fa_bwd_dq_d(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(o), P(d["do"]),
+                         P(lse), P(dvec), w.scale, c, P(dq), st))
 
     def dkdv():
         ck(L.fa_bwd_dkdv(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(d["do"]),
                          P(lse), P(dvec), w.scale, c, P(dk), P(dv), st))
 
-    def dqs():
-        ck(L.fa_bwd_dq(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(d["do"]),
-                       P(lse), P(dvec), w.scale, c, P(dq), st))
-
-    return (fwd, pre, dkdv, dqs), {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    return (fwd, dqs, dkdv), {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 
 def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0):
@@ -128,7 +127,7 @@ def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0):
         if done >= warmup:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    names = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
+    names = ("fwd", "bwd_dq", "bwd_dkdv")
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
           for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
@@ -435,7 +434,7 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": _traffic(kname, w.name),
                 "ms_per_launch": round(kern[dom], 4),
                 "flops_per_launch": kflops}
-    bwd_ms = kern["bwd_preprocess"] + kern["bwd_dkdv"] + kern["bwd_dq"]
+    bwd_ms = kern["bwd_dkdv"] + kern["bwd_dq"]
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "settle_s": args.settle, "ms_per_step": round(ms_step, 4),

@@ -76,6 +76,8 @@ def lib():
     L.fa_bwd_dkdv.restype = i
     L.fa_bwd_dq.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p]
     L.fa_bwd_dq.restype = i
+    L.fa_bwd_dq_d.argtypes = [i, i, i, i, i, p, p, p, p, p, p, p, f, i, p, p]
+    L.fa_bwd_dq_d.restype = i
     L.fa_std_row_stride.argtypes = [i]
     L.fa_std_row_stride.restype = i
     for name in ("fa_std_p_bytes", "fa_std_fwd_workspace_bytes", "fa_std_bwd_workspace_bytes"):
@@ -237,6 +239,14 @@ def bwd_dkdv(q, k, v, do, lse, dvec, dk, dv, scale=None, causal=False):
     dt, B, H, N, d = _check_qkv(q, k, v, do, dk, dv)
     _call("fa_bwd_dkdv", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
           _ptr(dvec), _scale(scale, d), int(bool(causal)), _ptr(dk), _ptr(dv), _stream(q))
+
+
+def bwd_dq_d(q, k, v, o, do, lse, dvec, dq, scale=None, causal=False):
+    """Stage 3 with stage 1 folded in: dQ, and dvec = rowsum(dO o O) written
+    for a bwd_dkdv that follows."""
+    dt, B, H, N, d = _check_qkv(q, k, v, o, do, dq)
+    _call("fa_bwd_dq_d", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+          _ptr(lse), _ptr(dvec), _scale(scale, d), int(bool(causal)), _ptr(dq), _stream(q))
 
 
 def bwd_dq(q, k, v, do, lse, dvec, dq, scale=None, causal=False):

@@ -258,6 +258,16 @@ int fa_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q, const void *
                                   (hipStream_t)stream));
 }
 
+int fa_bwd_dq_d(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                const void *V, const void *O, const void *dO, const float *LSE, float *Dvec,
+                float scale, int causal, void *dQ, void *stream) {
+  const int rc = check_sweep(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal);
+  if (rc != FA_OK) return rc;
+  if (!tensor_ok(O) || !tensor_ok(dQ)) return FA_ERR_INVALID_ARG;
+  return status(fa::launch_bwd_dq_fused(dtype, B, H, N, d, Q, K, V, O, dO, LSE, Dvec, scale,
+                                        causal, dQ, (hipStream_t)stream));
+}
+
 int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
            const void *O, const void *dO, const float *LSE, float scale, int causal, void *dQ,
            void *dK, void *dV, void *workspace, size_t workspace_bytes, void *stream) {
@@ -271,13 +281,13 @@ int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, 
   if (workspace_bytes < fa_bwd_workspace_bytes(dtype, B, H, N, d)) return FA_ERR_WORKSPACE;
   float *Dvec = (float *)workspace;
   hipStream_t st = (hipStream_t)stream;
-  if ((rc = status(fa::launch_bwd_preprocess(dtype, B, H, N, d, O, dO, Dvec, st))) != FA_OK)
+  // The dQ sweep forms D itself (as fa_bwd_preprocess would) and stores it
+  // for the dK/dV sweep that follows on the stream.
+  if ((rc = status(fa::launch_bwd_dq_fused(dtype, B, H, N, d, Q, K, V, O, dO, LSE, Dvec, scale,
+                                           causal, dQ, st))) != FA_OK)
     return rc;
-  if ((rc = status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
-                                       dK, dV, st))) != FA_OK)
-    return rc;
-  return status(
-      fa::launch_bwd_dq(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal, dQ, st));
+  return status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
+                                    dK, dV, st));
 }
 
 int fa_std_row_stride(int N) { return N > 0 ? fa::std_row_stride(N) : 0; }

@@ -34,6 +34,25 @@ namespace fa {
 // ---------------------------------------------------------------------------
 // D_i = sum_k dO_ik O_ik (fp32).
 // ---------------------------------------------------------------------------
+// The 8 products of one 16-byte chunk of O and dO, summed in element order
+// with explicit fmas. The preprocess kernel and the dQ sweep (which forms D
+// itself inside fa_bwd) both use it and reduce the chunks of a row in the
+// same tree, so both give the same D bit for bit.
+template <typename T>
+__device__ __forceinline__ float dot8(const u32x4 &a, const u32x4 &b) {
+  float acc = 0.f;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    acc = __builtin_fmaf(to_f32<T>((uint16_t)(a[h] & 0xffffu)),
+                         to_f32<T>((uint16_t)(b[h] & 0xffffu)), acc);
+    acc = __builtin_fmaf(to_f32<T>((uint16_t)(a[h] >> 16)), to_f32<T>((uint16_t)(b[h] >> 16)),
+                         acc);
+  }
+  return acc;
+}
+
+// Row sums over chunks: thread sub of a row holds chunk sub; the xor tree
+// adds chunk t and t ^ off for off = TPR/2, ..., 1.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict__ O,
                                                       const uint16_t *__restrict__ dO,
@@ -44,15 +63,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
   const long row = (long)blockIdx.x * RPB + tid / TPR;
   const int sub = tid % TPR;
   float acc = 0.f;
-  if (row < rows) {
-    const u32x4 a = ld128(O + row * D + 8 * sub);
-    const u32x4 b = ld128(dO + row * D + 8 * sub);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      acc += to_f32<T>((uint16_t)(a[h] & 0xffffu)) * to_f32<T>((uint16_t)(b[h] & 0xffffu));
-      acc += to_f32<T>((uint16_t)(a[h] >> 16)) * to_f32<T>((uint16_t)(b[h] >> 16));
-    }
-  }
+  if (row < rows) acc = dot8<T>(ld128(O + row * D + 8 * sub), ld128(dO + row * D + 8 * sub));
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
   if (row < rows && sub == 0) Dvec[row] = acc;
@@ -446,12 +457,12 @@ struct DqCfg {
 //
 // One block of query rows (block qb of slice bh). LDS buffer b: K tile at
 // kv + 2*b*TILE, V tile right after it.
-template <typename T, int D, int W, bool CAUSAL>
+template <typename T, int D, int W, bool CAUSAL, bool DFUSE>
 __device__ __forceinline__ void dq_block(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dQ,
-    int N, int bh, int qb, float c2, float scale, uint16_t *kv) {
+    const uint16_t *__restrict__ O, const float *__restrict__ LSE, float *__restrict__ Dvec,
+    uint16_t *__restrict__ dQ, int N, int bh, int qb, float c2, float scale, uint16_t *kv) {
   using C = DqCfg<D, W>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -472,7 +483,25 @@ __device__ __forceinline__ void dq_block(
     oreg[c] = ld128(dOh + (size_t)qld * D + 16 * c + 8 * g);
   }
   const float lse2 = LSE[(size_t)bh * N + qld] * kLog2e;
-  const float dd = Dvec[(size_t)bh * N + qld];
+  // D of this row: read, or (DFUSE) formed here from O and the dO chunks
+  // already in registers -- lane g holds chunks 2c + g, so the chunk tree of
+  // the preprocess kernel runs within the lane down to the last level, which
+  // joins the lane pair -- and stored for the dK/dV sweep.
+  float dd;
+  if constexpr (DFUSE) {
+    float part[C::NCH];
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c)
+      part[c] = dot8<T>(ld128(O + base + (size_t)qld * D + 16 * c + 8 * g), oreg[c]);
+#pragma unroll
+    for (int h = C::NCH / 2; h > 0; h >>= 1)
+#pragma unroll
+      for (int c = 0; c < h; ++c) part[c] = part[c] + part[c + h];
+    dd = pair_sum(part[0]);
+    if (qrow < N && g == 0) Dvec[(size_t)bh * N + qrow] = dd;
+  } else {
+    dd = Dvec[(size_t)bh * N + qld];
+  }
 
   const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
   const int ntiles = (kend + C::BC - 1) / C::BC;
@@ -628,25 +657,26 @@ __device__ __forceinline__ void dq_block(
 
 // Work units as in the forward: one query block, or under the causal mask
 // the pair (nqb - 1 - p, p) of blocks with equal total length.
-template <typename T, int D, int W, bool CAUSAL>
+template <typename T, int D, int W, bool CAUSAL, bool DFUSE>
 __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dQ,
-    int N, int nqb, int nunits, int total, float c2, float scale) {
+    const uint16_t *__restrict__ O, const float *__restrict__ LSE, float *__restrict__ Dvec,
+    uint16_t *__restrict__ dQ, int N, int nqb, int nunits, int total, float c2, float scale) {
   using C = DqCfg<D, W>;
   __shared__ __attribute__((aligned(1024))) uint16_t kv[4 * C::TILE];
   const int tile = xcd_tile(blockIdx.x, total);
   const int bh = tile / nunits;
   const int u = tile - bh * nunits;
   if (!CAUSAL) {
-    dq_block<T, D, W, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
+    dq_block<T, D, W, CAUSAL, DFUSE>(Q, K, V, dO, O, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
     return;
   }
-  dq_block<T, D, W, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, nqb - 1 - u, c2, scale, kv);
+  dq_block<T, D, W, CAUSAL, DFUSE>(Q, K, V, dO, O, LSE, Dvec, dQ, N, bh, nqb - 1 - u, c2, scale,
+                                   kv);
   if (u != nqb - 1 - u) {
     __syncthreads();  // every wave is done with the LDS tiles
-    dq_block<T, D, W, CAUSAL>(Q, K, V, dO, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
+    dq_block<T, D, W, CAUSAL, DFUSE>(Q, K, V, dO, O, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
   }
 }
 
@@ -676,6 +706,8 @@ struct BwdArgs {
   const uint16_t *Q, *K, *V, *dO;
   const float *LSE, *Dvec;
   float c2, scale;
+  const uint16_t *O;  // dQ sweep only: form D from O and dO (else null)
+  float *Dout;        // where that sweep writes D (else Dvec, read-only)
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -690,28 +722,33 @@ static hipError_t dkdv(const BwdArgs &a, void *dK, void *dV, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int W, bool CAUSAL>
+template <typename T, int D, int W, bool CAUSAL, bool DFUSE>
 static hipError_t dq_w(const BwdArgs &a, void *dQ, hipStream_t st) {
   using C = DqCfg<D, W>;
   const int nqb = (a.N + C::BR - 1) / C::BR;
   const int nunits = CAUSAL ? (nqb + 1) / 2 : nqb;
   const int total = nunits * a.BH;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, W, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
-                     a.Q, a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dQ, a.N, nqb, nunits, total,
-                     a.c2, a.scale);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, W, CAUSAL, DFUSE>), dim3(total), dim3(C::kThreads), 0,
+                     st, a.Q, a.K, a.V, a.dO, a.O, a.LSE, a.Dout, (uint16_t *)dQ, a.N, nqb,
+                     nunits, total, a.c2, a.scale);
   return hipGetLastError();
 }
 
+// Dvec read (a.Dvec) or, with a.O set, formed from O and dO and written to
+// a.Dout.
 template <typename T, int D, bool CAUSAL>
 static hipError_t dq(const BwdArgs &a, void *dQ, hipStream_t st) {
-  return use_256_row_blocks(a.BH, a.N, CAUSAL) ? dq_w<T, D, 8, CAUSAL>(a, dQ, st)
-                                               : dq_w<T, D, 4, CAUSAL>(a, dQ, st);
+  const bool w8 = use_256_row_blocks(a.BH, a.N, CAUSAL);
+  if (a.O != nullptr)
+    return w8 ? dq_w<T, D, 8, CAUSAL, true>(a, dQ, st) : dq_w<T, D, 4, CAUSAL, true>(a, dQ, st);
+  return w8 ? dq_w<T, D, 8, CAUSAL, false>(a, dQ, st) : dq_w<T, D, 4, CAUSAL, false>(a, dQ, st);
 }
 
 static BwdArgs bwd_args(int B, int H, int N, const void *Q, const void *K, const void *V,
                         const void *dO, const float *LSE, const float *Dvec, float scale) {
   return BwdArgs{B * H, N, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                 (const uint16_t *)dO, LSE, Dvec, scale * kLog2e, scale};
+                 (const uint16_t *)dO, LSE, Dvec, scale * kLog2e, scale, nullptr,
+                 const_cast<float *>(Dvec)};
 }
 
 // Instantiates F<T, D, CAUSAL>(args...) for the run-time dtype, d, causal.
@@ -737,6 +774,16 @@ hipError_t launch_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q, c
                          const void *V, const void *dO, const float *LSE, const float *Dvec,
                          float scale, int causal, void *dQ, hipStream_t st) {
   const BwdArgs a = bwd_args(B, H, N, Q, K, V, dO, LSE, Dvec, scale);
+  return FA_DISPATCH(dq, dtype, d, causal, a, dQ, st);
+}
+
+hipError_t launch_bwd_dq_fused(int dtype, int B, int H, int N, int d, const void *Q,
+                               const void *K, const void *V, const void *O, const void *dO,
+                               const float *LSE, float *Dvec, float scale, int causal, void *dQ,
+                               hipStream_t st) {
+  BwdArgs a = bwd_args(B, H, N, Q, K, V, dO, LSE, Dvec, scale);
+  a.O = (const uint16_t *)O;
+  a.Dout = Dvec;
   return FA_DISPATCH(dq, dtype, d, causal, a, dQ, st);
 }
 

@@ -62,4 +62,12 @@ hipError_t launch_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q, c
                          const void *V, const void *dO, const float *LSE, const float *Dvec,
                          float scale, int causal, void *dQ, hipStream_t stream);
 
+// dQ as launch_bwd_dq, with D formed from O and dO inside the sweep (the
+// same values launch_bwd_preprocess computes, bit for bit) and written to
+// Dvec for a dK/dV sweep launched after it.
+hipError_t launch_bwd_dq_fused(int dtype, int B, int H, int N, int d, const void *Q,
+                               const void *K, const void *V, const void *O, const void *dO,
+                               const float *LSE, float *Dvec, float scale, int causal, void *dQ,
+                               hipStream_t stream);
+
 }  // namespace fa

@@ -190,7 +190,9 @@ size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d);
  * are rounded to dtype before the products that consume them; all sums are
  * fp32. Deterministic: the same inputs give bit-identical dQ, dK and dV
  * (every output element is summed by one thread in a fixed order).
- * Enqueues, in order: fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq.
+ * Enqueues fa_bwd_dq_d (the dQ sweep, which also forms D into the
+ * workspace) and then fa_bwd_dkdv; the results equal fa_bwd_preprocess,
+ * fa_bwd_dkdv and fa_bwd_dq called in turn, bit for bit.
  */
 int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
            const void *V, const void *O, const void *dO, const float *LSE,
@@ -233,6 +235,20 @@ int fa_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q,
               const void *K, const void *V, const void *dO, const float *LSE,
               const float *Dvec, float scale, int causal, void *dQ,
               void *stream);
+
+/*
+ * fa_bwd_dq_d: fa_bwd_dq with D formed in the same sweep instead of read:
+ *   each workgroup forms Dvec for its own query rows from O and dO (the
+ *   values fa_bwd_preprocess writes, bit for bit: same products, same
+ *   summation tree), uses them and stores them, so that fa_bwd_dkdv can
+ *   follow it on the same stream without the preprocess pass. fa_bwd runs
+ *   this and then fa_bwd_dkdv.
+ *   In: Q, K, V, O, dO dtype; LSE fp32.  Out: dQ dtype; Dvec [B,H,N] fp32.
+ */
+int fa_bwd_dq_d(int dtype, int B, int H, int N, int d, const void *Q,
+                const void *K, const void *V, const void *O, const void *dO,
+                const float *LSE, float *Dvec, float scale, int causal,
+                void *dQ, void *stream);
 
 /*
  * Standard attention that stores the N x N matrices: the method the pages

@@ -113,6 +113,11 @@ def test_stage_entry_points_reject(L):
     assert L.fa_bwd_dq(2, 1, 1, 8, 64, A, A, A, A, A, A, -0.5, 0, A, None) == INVALID
     assert L.fa_bwd_dq(2, 1, 1, 8, 96, A, A, A, A, A, A, 0.5, 0, A, None) == UNSUP
     assert L.fa_bwd_dq(2, 1, 1, 8, 64, A, A, A, A, A, A, 0.5, 0, NUL, None) == INVALID
+    assert L.fa_bwd_dq_d(2, 1, 1, 8, 64, A, A, A, NUL, A, A, A, 0.5, 0, A, None) == INVALID
+    assert L.fa_bwd_dq_d(2, 1, 1, 8, 64, A, A, A, A, A, A, NUL, 0.5, 0, A, None) == INVALID
+    assert L.fa_bwd_dq_d(2, 1, 1, 8, 64, A, A, A, A, A, A, A, 0.5, 0, MIS, None) == INVALID
+    assert L.fa_bwd_dq_d(0, 1, 1, 8, 64, A, A, A, A, A, A, A, 0.5, 0, A, None) == UNSUP
+    assert L.fa_bwd_dq_d(2, 1, 1, 8, 64, A, A, A, A, A, A, A, 0.5, 2, A, None) == INVALID
 
 
 @pytest.mark.parametrize("dtype,B,H,N,d", [(2, 1, 1, 1, 64), (1, 2, 3, 1000, 128),

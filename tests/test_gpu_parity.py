@@ -249,7 +249,8 @@ def test_gradient_sums_and_determinism(fa, name):
 
 def test_stages_match_fused_call(fa):
     """fa_bwd equals its three stages called one by one, in either order of
-    the two gradient sweeps."""
+    the two gradient sweeps, and equals fa_bwd_dq_d then fa_bwd_dkdv; the D
+    that fa_bwd_dq_d forms equals fa_bwd_preprocess's bit for bit."""
     w = ai.custom("stages", 2, 4, 700, 128, "bf16", True, seed=11)
     d = _gpu(ai.make_inputs(w))
     o, lse = fa.fwd(d["q"], d["k"], d["v"], w.scale, True)
@@ -263,6 +264,13 @@ def test_stages_match_fused_call(fa):
     fa.bwd_dkdv(d["q"], d["k"], d["v"], d["do"], lse, dvec, dk2, dv2, w.scale, True)
     torch.cuda.synchronize()
     assert torch.equal(dk, dk2) and torch.equal(dv, dv2) and torch.equal(dq, dq2)
+    dvec3 = torch.full_like(dvec, float("nan"))
+    dk3, dv3, dq3 = torch.empty_like(dk), torch.empty_like(dv), torch.empty_like(dq)
+    fa.bwd_dq_d(d["q"], d["k"], d["v"], o, d["do"], lse, dvec3, dq3, w.scale, True)
+    fa.bwd_dkdv(d["q"], d["k"], d["v"], d["do"], lse, dvec3, dk3, dv3, w.scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(dvec3, dvec)
+    assert torch.equal(dk, dk3) and torch.equal(dv, dv3) and torch.equal(dq, dq3)
 
 
 def test_nan_in_query_row_stays_in_that_row(fa):
