@@ -13,6 +13,9 @@ Recipe (one line per workload):
     embedding (base 10000, position = row index, pairs (x_k, x_{k+d/2})),
     evaluated in fp64;
   * round to the dtype with round-to-nearest-even (torch's ``.to``).
+Tensors too large to draw on the host (``make_inputs_device``) are drawn the
+same way on the GPU from ``torch.Generator(device).manual_seed(seed)``, one
+tensor at a time (no rotary embedding, no scaling).
 
 The pages' own test harness (the attention-and-matrix-product essay, section 4)
 runs softmax attention on randn(1, 256, 64) with seed 42 and scale 64^-0.5;
@@ -121,4 +124,19 @@ def make_inputs(w: Workload, with_do: bool = True) -> dict:
            "v": v.to(dt).contiguous()}
     if do is not None:
         out["do"] = do.to(dt).contiguous()
+    return out
+
+
+def make_inputs_device(w: Workload, device: str = "cuda", with_do: bool = True) -> dict:
+    """Q, K, V (and dO) drawn on the device, for shapes too large for the host
+    path: each tensor i.i.d. N(0, 1) in fp32 in the order Q, K, V, dO, then
+    rounded to w's dtype before the next is drawn."""
+    if w.rope or w.qkv_std != 1.0 or w.do_std != 1.0:
+        raise ValueError("device-drawn inputs take the plain N(0, 1) recipe only")
+    g = torch.Generator(device=device).manual_seed(w.seed)
+    shape = (w.B, w.H, w.N, w.d)
+    out = {}
+    for name in ("q", "k", "v", "do") if with_do else ("q", "k", "v"):
+        out[name] = torch.randn(shape, generator=g, dtype=torch.float32,
+                                device=device).to(w.torch_dtype)
     return out

@@ -21,8 +21,10 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Checks shared by every entry point. Returns FA_OK or an error code.
 int check_shape(int dtype, int B, int H, int N, int d, bool bwd) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
-  const long long elems = (long long)B * H * N * d;
-  if (elems >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+  // Rows (and so workgroup counts) fit in int; one slice fits in the 32-bit
+  // byte range of a buffer resource. Offsets into whole tensors are 64-bit.
+  if ((long long)B * H * N >= (1LL << 31) || (long long)N * d >= (1LL << 31))
+    return FA_ERR_INVALID_ARG;
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (bwd && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -97,6 +99,9 @@ int run_split(int dtype, int B, int H, int Nq, int Nk, int d, const void *Q, con
   if (nsplit < 0 || nsplit > kMaxSplit) return FA_ERR_INVALID_ARG;
   const int req = nsplit == 0 ? auto_split(B, H, Nq, Nk) : nsplit;
   const int parts = fa::split_parts(Nk, req);
+  // One workgroup per slice, key range and 128-row query block: at most
+  // B*H*Nq/2 + B*H*parts with parts <= min(64, Nk/64), below 2^31 given
+  // the row limits that check_shape put on Nq and Nk.
   if (workspace_bytes < split_bytes(parts, B, H, Nq, d)) return FA_ERR_WORKSPACE;
   float *Op = (float *)workspace;
   float *Lp = (float *)((char *)workspace + split_o_bytes(parts, B, H, Nq, d));

@@ -26,7 +26,9 @@
  *   layout   Q, K, V, O, dO, dQ, dK, dV are dense [B, H, N, d] arrays, d
  *            fastest (row n of slice (b, h) starts at ((b*H + h)*N + n)*d).
  *            LSE and D are dense fp32 [B, H, N].
- *   sizes    B >= 1, H >= 1, N >= 1, d in {64, 128}; B*H*N*d < 2^31.
+ *   sizes    B >= 1, H >= 1, N >= 1, d in {64, 128}; B*H*N < 2^31 rows and
+ *            N*d < 2^31 (one slice within 4 GiB). A tensor may exceed
+ *            4 GiB: offsets into whole tensors are 64-bit.
  *   causal   0: every query sees every key. 1: query i sees keys j <= i
  *            (top-left aligned; queries and keys have the same length N).
  *   scale    finite and > 0; the pages use 1/sqrt(d). S = scale * Q K^T.
@@ -63,7 +65,7 @@ extern "C" {
 #define FA_OK 0
 #define FA_ERR_INVALID_ARG (-1) /* null or misaligned pointer, size <= 0,
                                    scale not finite and > 0, causal not 0/1,
-                                   B*H*N*d too large */
+                                   B*H*N or N*d too large */
 #define FA_ERR_UNSUPPORTED (-2) /* head size d or dtype not built */
 #define FA_ERR_WORKSPACE (-3)   /* workspace smaller than required */
 #define FA_ERR_LAUNCH (-4)      /* kernel launch failed */

@@ -76,7 +76,9 @@ def fwd(L, dtype=2, B=1, H=1, N=16, d=64, q=A, k=A, v=A, scale=0.125, causal=0, 
     (dict(q=NUL), INVALID), (dict(k=NUL), INVALID), (dict(v=NUL), INVALID),
     (dict(o=NUL), INVALID), (dict(lse=NUL), INVALID),
     (dict(q=MIS), INVALID), (dict(o=MIS), INVALID),
-    (dict(B=1 << 12, H=1 << 12, N=1 << 10, d=128), INVALID),  # > 2^31 elements
+    (dict(B=1 << 12, H=1 << 12, N=1 << 10, d=128), INVALID),  # 2^34 rows
+    (dict(B=1 << 16, H=1 << 15, N=1, d=64), INVALID),  # B*H*N = 2^31 rows
+    (dict(B=1, H=1, N=1 << 24, d=128), INVALID),  # one slice of 2^31 elements
 ])
 def test_fwd_rejects(L, kw, code):
     assert fwd(L, **kw) == code
@@ -121,13 +123,15 @@ def test_stage_entry_points_reject(L):
 
 
 @pytest.mark.parametrize("dtype,B,H,N,d", [(2, 1, 1, 1, 64), (1, 2, 3, 1000, 128),
-                                          (2, 16, 32, 2048, 128)])
+                                          (2, 16, 32, 2048, 128),
+                                          (2, 41, 400, 1024, 128)])  # tensors past 4 GiB
 def test_workspace_bytes(L, dtype, B, H, N, d):
     """fp32 D [B,H,N] rounded up to 256 bytes."""
     dbytes = -(-B * H * N * 4 // 256) * 256
     assert L.fa_bwd_workspace_bytes(dtype, B, H, N, d) == dbytes
     assert L.fa_bwd_workspace_bytes(0, B, H, N, d) == 0     # fp32: no backward
     assert L.fa_bwd_workspace_bytes(dtype, B, H, N, 80) == 0
+    assert L.fa_bwd_workspace_bytes(dtype, 1 << 16, 1 << 15, 1, d) == 0  # 2^31 rows
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
