@@ -1,8 +1,8 @@
 """Throughput benchmark: exact attention forward + backward on one MI355X.
 
 One step is one pass of the whole path over one batch: fa_fwd (O, LSE), then
-fa_bwd's three stages (D = rowsum(dO o O), the dK/dV sweep over key blocks,
-the dQ sweep over query blocks). The workload is the Llama-2-7B-shaped causal attention layer
+fa_bwd's two stages as it issues them (the dQ sweep over query blocks, which
+also forms D = rowsum(dO o O), then the dK/dV sweep over key blocks). The workload is the Llama-2-7B-shaped causal attention layer
 (batch 16, 32 heads, N = 2048, d = 128, bf16; rotary Q/K, dO ~ N(0, 0.01)),
 with inputs resident in device memory before the timed region.
 
@@ -31,12 +31,17 @@ Prints ONE JSON line. Besides the required keys it carries:
   kvcache       fa_fwd_kvcache: decoding (one new query per slice over an
                 8192-key cache; HBM-bound, reported in GB/s of K and V read)
                 and chunked prefill (512 new queries over 8192 keys).
+  gpu_clock     graphics clock (mean over the XCDs) and socket power sampled
+                with amd-smi while the main workload runs (after its first
+                half second), and the dense bf16 MFMA rate at that clock.
 """
 import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -109,7 +114,67 @@ def _step_fns(fa, torch, w, d):
     return (fwd, dqs, dkdv), {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 
-def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0):
+class ClockSampler:
+    """Samples GPU 0's graphics clocks and socket power with amd-smi in a
+    background thread (a child process per sample; nothing touches the GPU
+    from here). Samples from the first `skip_s` seconds are dropped: the
+    clock is still climbing from idle then."""
+
+    CMD = ["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"]
+
+    def __init__(self, period_s=0.2, skip_s=0.5):
+        self.period_s, self.skip_s = period_s, skip_s
+        self.samples, self.error = [], None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _parse(text):
+        starts = [i for i in (text.find("{"), text.find("[")) if i >= 0]
+        data = json.loads(text[min(starts):] if starts else text)
+        if isinstance(data, dict):
+            data = data.get("gpu_data", [data])
+        g = data[0]
+        clks = [v["clk"]["value"] for k, v in g["clock"].items()
+                if k.startswith("gfx_") and isinstance(v, dict)
+                and isinstance(v.get("clk", {}).get("value"), (int, float))]
+        pw = g.get("power", {}).get("socket_power", {}).get("value")
+        return (sum(clks) / len(clks) if clks else None,
+                pw if isinstance(pw, (int, float)) else None)
+
+    def _run(self):
+        t0 = time.perf_counter()
+        while not self._stop.is_set():
+            try:
+                r = subprocess.run(self.CMD, capture_output=True, text=True, timeout=5)
+                clk, pw = self._parse(r.stdout)
+                if time.perf_counter() - t0 >= self.skip_s and clk is not None:
+                    self.samples.append((clk, pw))
+            except Exception as e:  # no amd-smi, or output it cannot parse
+                self.error = "%s: %s" % (type(e).__name__, e)
+                return
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join(timeout=10)
+        if not self.samples:
+            return {"samples": 0, "error": self.error or "no sample"}
+        clk = sorted(c for c, _ in self.samples)
+        pw = sorted(p for _, p in self.samples if p is not None)
+        med = clk[len(clk) // 2]
+        # 256 CUs x 4 SIMDs x 1024 bf16 flops per clock.
+        return {"gfx_mhz": round(med, 1), "gfx_mhz_min": round(clk[0], 1),
+                "gfx_mhz_max": round(clk[-1], 1),
+                "socket_power_w": pw[len(pw) // 2] if pw else None,
+                "samples": len(clk), "tool": " ".join(self.CMD),
+                "mfma_bf16_tflops_at_clock": round(256 * 4 * 1024 * med * 1e6 / 1e12, 1)}
+
+
+def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0, sampler=None):
     """Returns (ms_per_step, ms_fwd_only, per-kernel ms dict, outputs, host inputs).
 
     After the `warmup` steps, further untimed steps run until `settle_s`
@@ -118,6 +183,8 @@ def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0):
     steps should see the clock a sustained run gets."""
     d, host = _inputs(w, torch, "cuda")
     fns, outs = _step_fns(fa, torch, w, d)
+    if sampler is not None:
+        sampler.start()
     t_start = time.perf_counter()
     done = 0
     while done < warmup or time.perf_counter() - t_start < settle_s:
@@ -143,6 +210,8 @@ def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0):
             ev[s][-1].record()
     t1.record()
     torch.cuda.synchronize()
+    if sampler is not None:
+        sampler.clock = sampler.stop()
     ms_step = t0.elapsed_time(t1) / steps
     kern = None
     if per_kernel:
@@ -417,8 +486,9 @@ def main():
     fa.lib()
 
     w = ai.WORKLOADS[args.workload]
+    sampler = ClockSampler()
     ms_step, ms_fwd, kern, outs, host = time_workload(fa, torch, w, args.steps, args.warmup,
-                                                       settle_s=args.settle)
+                                                       settle_s=args.settle, sampler=sampler)
     flops_step = w.fwd_flops() + w.bwd_flops()
     value = flops_step / (ms_step * 1e-3) / 1e12
     fwd_tflops = w.fwd_flops() / (ms_fwd * 1e-3) / 1e12
@@ -449,7 +519,11 @@ def main():
            "fwd_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
            "fwdbwd_frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
            "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
-           "roofline": roofline}
+           "roofline": roofline,
+           "gpu_clock": sampler.clock}
+    if sampler.clock.get("mfma_bf16_tflops_at_clock"):
+        roofline["frac_of_peak_at_measured_clock"] = round(
+            achieved / sampler.clock["mfma_bf16_tflops_at_clock"], 4)
 
     if not args.no_cpu:
         cb, worst = cpu_baseline(w, host, outs)
