@@ -535,7 +535,7 @@ def main():
                      "perf-8k-causal", "c3", "c4"):
             ws = ai.WORKLOADS[name]
             s_ms, f_ms, _, _, _ = time_workload(fa, torch, ws, 10, 3, per_kernel=False,
-                                                  settle_s=min(args.settle, 0.5))
+                                                  settle_s=min(args.settle, 1.0))
             tf = (ws.fwd_flops() + ws.bwd_flops()) / (s_ms * 1e-3) / 1e12
             ff = ws.fwd_flops() / (f_ms * 1e-3) / 1e12
             sweep.append({"workload": name, "B": ws.B, "H": ws.H, "N": ws.N, "d": ws.d,
