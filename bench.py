@@ -458,6 +458,9 @@ def main():
     ap.add_argument("--no-kvcache", action="store_true")
     ap.add_argument("--no-std", action="store_true",
                     help="skip the stored-P standard-attention comparison")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="do not sample the clock with amd-smi (under a profiler, whose "
+                         "preloaded library would start the GPU in every child process)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales the HBM "
                          "byte counters read under rocprofv3)")
@@ -486,9 +489,10 @@ def main():
     fa.lib()
 
     w = ai.WORKLOADS[args.workload]
-    sampler = ClockSampler()
+    sampler = None if args.no_clock else ClockSampler()
     ms_step, ms_fwd, kern, outs, host = time_workload(fa, torch, w, args.steps, args.warmup,
                                                        settle_s=args.settle, sampler=sampler)
+    clock = sampler.clock if sampler is not None else {"samples": 0, "error": "--no-clock"}
     flops_step = w.fwd_flops() + w.bwd_flops()
     value = flops_step / (ms_step * 1e-3) / 1e12
     fwd_tflops = w.fwd_flops() / (ms_fwd * 1e-3) / 1e12
@@ -520,10 +524,10 @@ def main():
            "fwdbwd_frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
            "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
            "roofline": roofline,
-           "gpu_clock": sampler.clock}
-    if sampler.clock.get("mfma_bf16_tflops_at_clock"):
+           "gpu_clock": clock}
+    if clock.get("mfma_bf16_tflops_at_clock"):
         roofline["frac_of_peak_at_measured_clock"] = round(
-            achieved / sampler.clock["mfma_bf16_tflops_at_clock"], 4)
+            achieved / clock["mfma_bf16_tflops_at_clock"], 4)
 
     if not args.no_cpu:
         cb, worst = cpu_baseline(w, host, outs)

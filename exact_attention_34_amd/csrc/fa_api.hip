@@ -56,10 +56,22 @@ int auto_split(int B, int H, int Nq, int Nk) {
   if (hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
     cus = v;
-  const long units = (long)B * H * ((Nq + 127) / 128);
-  long ns = (2L * cus + units - 1) / units;
-  const long tiles = (Nk + 63) / 64;
-  if (ns > tiles / 16) ns = tiles / 16;
+  long ns;
+  if (Nq == 1) {
+    // Decoding (vector kernel, HBM-bound): about one workgroup of four waves
+    // per compute unit, ranges of at least 256 keys. Measured at d = 128 over
+    // 1 to 64 ranges: K/V read rates peak (5.1-6.0 TB/s) at 256-512
+    // workgroups and fall with more (B1 H32 Nk32768: 8 ranges 5.10 TB/s,
+    // 32 ranges 4.34; B16 H32 Nk8192: 1 range 5.84, 16 ranges 5.66).
+    const long bh = (long)B * H;
+    ns = (cus + bh - 1) / bh;
+    if (ns > Nk / 256) ns = Nk / 256;
+  } else {
+    const long units = (long)B * H * ((Nq + 127) / 128);
+    ns = (2L * cus + units - 1) / units;
+    const long tiles = (Nk + 63) / 64;
+    if (ns > tiles / 16) ns = tiles / 16;
+  }
   if (ns > kMaxSplit) ns = kMaxSplit;
   return ns < 1 ? 1 : (int)ns;
 }

@@ -724,6 +724,137 @@ static hipError_t fwd_b16_c(int causal, int BH, int N, const void *Q, const void
                 : fwd_b16<T, D, false>(BH, N, Q, K, V, c2, O, LSE, st);
 }
 
+// ---------------------------------------------------------------------------
+// Decoding: one new query per slice (Nq = 1) over one range of cached keys.
+// ---------------------------------------------------------------------------
+// Per key the work is a d-element dot product and a d-element update of O,
+// so reading K and V from HBM bounds the kernel, and a matrix product would
+// fill one of its 32 rows. It runs on the vector units instead. A key row is
+// D/8 lanes x 16 bytes; per batch each wave issues 8 loads of K and 8 of V
+// per lane (KPB keys, all in flight before the first is used), forms the
+// scores with a butterfly sum inside each lane group, and applies the online
+// softmax ("Flash Attention" notes, section 2, part 4.2) once per batch:
+// running max m (base 2), normaliser l and unnormalised O, each lane group
+// holding its own keys' share of O for the 8 dims of its lanes. At the end
+// the lane groups, then the four waves, are combined with the same rescaling,
+// and the range's O / l and LSE go to the split workspace for
+// lse_merge_kernel. P stays in fp32: no matrix product consumes it.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, float *__restrict__ Op, float *__restrict__ Lp, int Nk,
+    int BH, int nparts, int split_keys, float c2) {
+  constexpr int LPR = D / 8;     // lanes per key row, 8 elements each
+  constexpr int KPI = 64 / LPR;  // keys per load instruction: one per lane group
+  constexpr int NL = 8;          // loads per tensor per batch
+  constexpr int KPB = KPI * NL;  // keys per wave per batch
+  __shared__ float red[4][D + 2];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bh = blockIdx.x / nparts, sp = blockIdx.x - bh * nparts;
+  const int kf = sp * split_keys, kl = min(Nk, kf + split_keys);
+  const int sub = lane % LPR, grp = lane / LPR;
+  const uint16_t *Kh = K + (size_t)bh * Nk * D + 8 * sub;
+  const uint16_t *Vh = V + (size_t)bh * Nk * D + 8 * sub;
+  // This lane's 8 query elements, times scale * log2(e): scores in base 2.
+  float qf[8];
+  {
+    const u32x4 qv = ld128(Q + (size_t)bh * D + 8 * sub);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      qf[2 * h] = to_f32<T>((uint16_t)(qv[h] & 0xffffu)) * c2;
+      qf[2 * h + 1] = to_f32<T>((uint16_t)(qv[h] >> 16)) * c2;
+    }
+  }
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  for (int k0 = kf + w * KPB; k0 < kl; k0 += 4 * KPB) {
+    u32x4 kr[NL], vr[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      // Keys past the range read its last row again (masked below).
+      const size_t key = (size_t)min(k0 + i * KPI + grp, kl - 1);
+      kr[i] = ld128(Kh + key * D);
+      vr[i] = ld128(Vh + key * D);
+    }
+    float s[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float a = 0.f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        a = __builtin_fmaf(to_f32<T>((uint16_t)(kr[i][h] & 0xffffu)), qf[2 * h], a);
+        a = __builtin_fmaf(to_f32<T>((uint16_t)(kr[i][h] >> 16)), qf[2 * h + 1], a);
+      }
+      s[i] = a;
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) s[i] += __shfl_xor(s[i], off, LPR);
+    // Key k0 (lane group 0, load 0) is in the range, so the batch max is finite.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      if (k0 + i * KPI + grp >= kl) s[i] = -INFINITY;
+      mx = fmaxf(mx, s[i]);
+    }
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float mn = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mn);  // 0 on the first batch (m = -inf)
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      s[i] = fast_exp2(s[i] - mn);
+      ps += s[i];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        o[2 * h] = __builtin_fmaf(s[i], to_f32<T>((uint16_t)(vr[i][h] & 0xffffu)), o[2 * h]);
+        o[2 * h + 1] = __builtin_fmaf(s[i], to_f32<T>((uint16_t)(vr[i][h] >> 16)), o[2 * h + 1]);
+      }
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) ps += __shfl_xor(ps, off);
+    l = l * alpha + ps;
+    m = mn;
+  }
+  // The lane groups share m and l; sum their O, then combine the waves.
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], off);
+  if (grp == 0)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[w][8 * sub + e] = o[e];
+  if (lane == 0) {
+    red[w][D] = m;
+    red[w][D + 1] = l;
+  }
+  __syncthreads();
+  if (tid < D) {
+    // A wave without keys has m = -inf, l = 0, O = 0 and weighs nothing;
+    // wave 0 always has keys (the range is not empty).
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) M = fmaxf(M, red[v][D]);
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float f = fast_exp2(red[v][D] - M);
+      L += red[v][D + 1] * f;
+      acc += red[v][tid] * f;
+    }
+    const size_t row = (size_t)sp * BH + bh;
+    Op[row * D + tid] = acc / L;
+    if (tid == 0) Lp[row] = (M + fast_log2(L)) * kLn2;
+  }
+}
+
 struct SplitArgs {
   int BH, Nq, Nk, qoff;
   const void *Q, *K, *V;
@@ -753,6 +884,25 @@ hipError_t launch_fwd_split(int dtype, int B, int H, int Nq, int Nk, int d, cons
                             float *Op, float *Lp, hipStream_t st) {
   const SplitArgs a{B * H, Nq, Nk, causal ? Nk - Nq : 0, Q, K, V, scale * kLog2e, Op, Lp,
                     split_parts(Nk, nsplit), split_key_count(Nk, nsplit)};
+  if (Nq == 1) {
+    // One query per slice (it sees every key, masked or not): the vector
+    // kernel, one workgroup per slice and key range.
+    const dim3 grid((unsigned)(a.BH * a.nsplit));
+    const auto q = (const uint16_t *)Q, k = (const uint16_t *)K, v = (const uint16_t *)V;
+    if (dtype == kBF16 && d == 128)
+      hipLaunchKernelGGL((decode_kernel<BF16, 128>), grid, dim3(256), 0, st, q, k, v, Op, Lp, Nk,
+                         a.BH, a.nsplit, a.split_keys, a.c2);
+    else if (dtype == kBF16)
+      hipLaunchKernelGGL((decode_kernel<BF16, 64>), grid, dim3(256), 0, st, q, k, v, Op, Lp, Nk,
+                         a.BH, a.nsplit, a.split_keys, a.c2);
+    else if (d == 128)
+      hipLaunchKernelGGL((decode_kernel<F16, 128>), grid, dim3(256), 0, st, q, k, v, Op, Lp, Nk,
+                         a.BH, a.nsplit, a.split_keys, a.c2);
+    else
+      hipLaunchKernelGGL((decode_kernel<F16, 64>), grid, dim3(256), 0, st, q, k, v, Op, Lp, Nk,
+                         a.BH, a.nsplit, a.split_keys, a.c2);
+    return hipGetLastError();
+  }
   if (dtype == kBF16)
     return d == 64 ? fwd_split_c<BF16, 64>(causal, a, st) : fwd_split_c<BF16, 128>(causal, a, st);
   return d == 64 ? fwd_split_c<F16, 64>(causal, a, st) : fwd_split_c<F16, 128>(causal, a, st);

@@ -137,6 +137,7 @@ int fa_fwd_splitkv_parts(int B, int H, int N, int nsplit);
  * Out: O [B, H, Nq, d] dtype, LSE [B, H, Nq] fp32.
  * Runs as fa_fwd_splitkv does (key ranges swept by separate workgroups, then
  * fa_lse_merge); nsplit and workspace as there, with its own size function.
+ * With Nq = 1 (decoding) the ranges run on a vector kernel, P in fp32.
  */
 int fa_fwd_kvcache(int dtype, int B, int H, int Nq, int Nk, int d,
                    const void *Q, const void *K, const void *V, float scale,

@@ -56,6 +56,25 @@ def test_kvcache_matches_oracle(fa, oracle_lib, dt, d, causal, Nq, Nk, nsplit):
                   what="kvcache Nq%d Nk%d" % (Nq, Nk))
 
 
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("Nk,nsplit", [(33, 0), (300, 1), (5000, 0), (5000, 7), (20000, 0)])
+def test_decode_many_slices(fa, oracle_lib, dt, d, Nk, nsplit):
+    """One new query per slice (the vector decoding kernel): 15 slices, key
+    ranges from one partial batch to many per wave, against the oracle on
+    every slice."""
+    B, H = 3, 5
+    q, k, v = _qkv(B, H, 1, Nk, d, dt, seed=Nk + nsplit + d)
+    o, lse = fa.fwd_kvcache(q.cuda(), k.cuda(), v.cuda(), d ** -0.5, True, nsplit)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            o_ref, l_ref = oracle_lib.attention_fwd_rows(f64(q[b, h]), np.array([Nk - 1]),
+                                                         f64(k[b, h]), f64(v[b, h]), d ** -0.5,
+                                                         True)
+            check_fwd(dt, f64(o[b, h]), f64(lse[b, h]), o_ref, l_ref,
+                      what="decode Nk%d nsplit%d" % (Nk, nsplit))
+
+
 def test_kvcache_equals_fwd_when_nq_equals_nk(fa):
     """Nq = Nk with the causal mask is the ordinary causal forward."""
     w = ai.custom("kv-eq", 2, 3, 650, 128, "bf16", True, seed=5)
