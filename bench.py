@@ -33,7 +33,10 @@ Prints ONE JSON line. Besides the required keys it carries:
                 and chunked prefill (512 new queries over 8192 keys).
   gpu_clock     graphics clock (mean over the XCDs) and socket power sampled
                 with amd-smi while the main workload runs (after its first
-                half second), and the dense bf16 MFMA rate at that clock.
+                0.8 s), and the dense bf16 MFMA rate at that clock.
+  kernels       each kernel of the step: mean launch time (HIP events), the
+                flops it executes and those the pages' count credits to it,
+                and both rates as TFLOP/s and as a fraction of the peak.
 """
 import argparse
 import hashlib
@@ -122,7 +125,7 @@ class ClockSampler:
 
     CMD = ["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"]
 
-    def __init__(self, period_s=0.2, skip_s=0.5):
+    def __init__(self, period_s=0.2, skip_s=0.8):
         self.period_s, self.skip_s = period_s, skip_s
         self.samples, self.error = [], None
         self._stop = threading.Event()
@@ -509,6 +512,21 @@ def main():
                 "ms_per_launch": round(kern[dom], 4),
                 "flops_per_launch": kflops}
     bwd_ms = kern["bwd_dkdv"] + kern["bwd_dq"]
+    # Executed MFMA work per launch: forward S and P V (4 N^2 d), dK/dV sweep
+    # S, dP, dV, dK (8 N^2 d), dQ sweep S, dP, dQ (6 N^2 d); halved when
+    # causal. Credited work is the pages' count (4 and 10 N^2 d), the
+    # backward split 8 : 2 as above.
+    unit = w.fwd_flops() / 4
+    per = {"fwd": (4 * unit, w.fwd_flops()), "bwd_dq": (6 * unit, 0.2 * w.bwd_flops()),
+           "bwd_dkdv": (8 * unit, 0.8 * w.bwd_flops())}
+    kernels = {}
+    for k, (ex, cr) in per.items():
+        t = kern[k] * 1e-3
+        kernels[k] = {"ms": round(kern[k], 4),
+                      "executed_tflops": round(ex / t / 1e12, 1),
+                      "credited_tflops": round(cr / t / 1e12, 1),
+                      "executed_frac": round(ex / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "credited_frac": round(cr / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "settle_s": args.settle, "ms_per_step": round(ms_step, 4),
@@ -523,6 +541,7 @@ def main():
            "fwd_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
            "fwdbwd_frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
            "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+           "kernels": kernels,
            "roofline": roofline,
            "gpu_clock": clock}
     if clock.get("mfma_bf16_tflops_at_clock"):
