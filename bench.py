@@ -32,8 +32,9 @@ Prints ONE JSON line. Besides the required keys it carries:
                 8192-key cache; HBM-bound, reported in GB/s of K and V read)
                 and chunked prefill (512 new queries over 8192 keys).
   gpu_clock     graphics clock (mean over the XCDs) and socket power sampled
-                with amd-smi while the main workload runs (after its first
-                0.8 s), and the dense bf16 MFMA rate at that clock.
+                with amd-smi while the main workload runs (settle, timed and
+                forward-only launches, after the first 0.8 s), and the dense
+                bf16 MFMA rate at that clock.
   kernels       each kernel of the step: mean launch time (HIP events), the
                 flops it executes and those the pages' count credits to it,
                 and both rates as TFLOP/s and as a fraction of the peak.
@@ -213,8 +214,6 @@ def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0, sa
             ev[s][-1].record()
     t1.record()
     torch.cuda.synchronize()
-    if sampler is not None:
-        sampler.clock = sampler.stop()
     ms_step = t0.elapsed_time(t1) / steps
     kern = None
     if per_kernel:
@@ -233,6 +232,10 @@ def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0, sa
     for f in fns:
         f()
     torch.cuda.synchronize()
+    # Stopped only now: joining the thread can take a sample's time, and an
+    # idle GPU lowers its clock before the forward-only launches above.
+    if sampler is not None:
+        sampler.clock = sampler.stop()
     return ms_step, ms_fwd, kern, outs, host
 
 

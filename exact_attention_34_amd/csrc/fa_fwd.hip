@@ -738,12 +738,14 @@ static hipError_t fwd_b16_c(int causal, int BH, int N, const void *Q, const void
 // holding its own keys' share of O for the 8 dims of its lanes. At the end
 // the lane groups, then the four waves, are combined with the same rescaling,
 // and the range's O / l and LSE go to the split workspace for
-// lse_merge_kernel. P stays in fp32: no matrix product consumes it.
+// lse_merge_kernel -- or, with a single range (Od set), straight to O
+// (rounded to T) and LSE. P stays in fp32: no matrix product consumes it.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, float *__restrict__ Op, float *__restrict__ Lp, int Nk,
-    int BH, int nparts, int split_keys, float c2) {
+    const uint16_t *__restrict__ V, float *__restrict__ Op, float *__restrict__ Lp,
+    uint16_t *__restrict__ Od, float *__restrict__ Ld, int Nk, int BH, int nparts,
+    int split_keys, float c2) {
   constexpr int LPR = D / 8;     // lanes per key row, 8 elements each
   constexpr int KPI = 64 / LPR;  // keys per load instruction: one per lane group
   constexpr int NL = 8;          // loads per tensor per batch
@@ -849,9 +851,15 @@ __global__ __launch_bounds__(256) void decode_kernel(
       L += red[v][D + 1] * f;
       acc += red[v][tid] * f;
     }
-    const size_t row = (size_t)sp * BH + bh;
-    Op[row * D + tid] = acc / L;
-    if (tid == 0) Lp[row] = (M + fast_log2(L)) * kLn2;
+    const float lse = (M + fast_log2(L)) * kLn2;
+    if (Od != nullptr) {
+      Od[(size_t)bh * D + tid] = (uint16_t)(pack2<T>(acc / L, 0.f) & 0xffffu);
+      if (tid == 0) Ld[bh] = lse;
+    } else {
+      const size_t row = (size_t)sp * BH + bh;
+      Op[row * D + tid] = acc / L;
+      if (tid == 0) Lp[row] = lse;
+    }
   }
 }
 
@@ -881,7 +889,7 @@ static hipError_t fwd_split_c(int causal, const SplitArgs &a, hipStream_t st) {
 
 hipError_t launch_fwd_split(int dtype, int B, int H, int Nq, int Nk, int d, const void *Q,
                             const void *K, const void *V, float scale, int causal, int nsplit,
-                            float *Op, float *Lp, hipStream_t st) {
+                            float *Op, float *Lp, void *O, float *LSE, hipStream_t st) {
   const SplitArgs a{B * H, Nq, Nk, causal ? Nk - Nq : 0, Q, K, V, scale * kLog2e, Op, Lp,
                     split_parts(Nk, nsplit), split_key_count(Nk, nsplit)};
   if (Nq == 1) {
@@ -889,18 +897,19 @@ hipError_t launch_fwd_split(int dtype, int B, int H, int Nq, int Nk, int d, cons
     // kernel, one workgroup per slice and key range.
     const dim3 grid((unsigned)(a.BH * a.nsplit));
     const auto q = (const uint16_t *)Q, k = (const uint16_t *)K, v = (const uint16_t *)V;
+    const auto od = (uint16_t *)O;
     if (dtype == kBF16 && d == 128)
-      hipLaunchKernelGGL((decode_kernel<BF16, 128>), grid, dim3(256), 0, st, q, k, v, Op, Lp, Nk,
-                         a.BH, a.nsplit, a.split_keys, a.c2);
+      hipLaunchKernelGGL((decode_kernel<BF16, 128>), grid, dim3(256), 0, st, q, k, v, Op, Lp, od,
+                         LSE, Nk, a.BH, a.nsplit, a.split_keys, a.c2);
     else if (dtype == kBF16)
-      hipLaunchKernelGGL((decode_kernel<BF16, 64>), grid, dim3(256), 0, st, q, k, v, Op, Lp, Nk,
-                         a.BH, a.nsplit, a.split_keys, a.c2);
+      hipLaunchKernelGGL((decode_kernel<BF16, 64>), grid, dim3(256), 0, st, q, k, v, Op, Lp, od,
+                         LSE, Nk, a.BH, a.nsplit, a.split_keys, a.c2);
     else if (d == 128)
-      hipLaunchKernelGGL((decode_kernel<F16, 128>), grid, dim3(256), 0, st, q, k, v, Op, Lp, Nk,
-                         a.BH, a.nsplit, a.split_keys, a.c2);
+      hipLaunchKernelGGL((decode_kernel<F16, 128>), grid, dim3(256), 0, st, q, k, v, Op, Lp, od,
+                         LSE, Nk, a.BH, a.nsplit, a.split_keys, a.c2);
     else
-      hipLaunchKernelGGL((decode_kernel<F16, 64>), grid, dim3(256), 0, st, q, k, v, Op, Lp, Nk,
-                         a.BH, a.nsplit, a.split_keys, a.c2);
+      hipLaunchKernelGGL((decode_kernel<F16, 64>), grid, dim3(256), 0, st, q, k, v, Op, Lp, od,
+                         LSE, Nk, a.BH, a.nsplit, a.split_keys, a.c2);
     return hipGetLastError();
   }
   if (dtype == kBF16)
