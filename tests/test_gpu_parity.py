@@ -195,6 +195,21 @@ def test_one_key_far_above_the_rest(fa, oracle_lib, dt, causal):
     _compare_slices(oracle_lib, w, inp, got, [(0, 0), (0, 1)], False)
 
 
+@pytest.mark.parametrize("scale", [1e-3, 4.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_extreme_scales(fa, oracle_lib, scale, causal):
+    """scale = 1e-3 (P nearly uniform: O near the mean of the visible V rows)
+    and scale = 4 (scores spread over hundreds of units: P nearly one-hot and
+    the reference moves often), forward and backward, bf16 d = 128."""
+    import types
+    base = ai.custom("scale-%g-%s" % (scale, "c" if causal else "nc"), 1, 2, 700, 128, "bf16",
+                     causal, seed=95)
+    w = types.SimpleNamespace(name=base.name, scale=scale, causal=causal, dtype=base.dtype)
+    inp = ai.make_inputs(base)
+    got = _run(fa, w, inp)
+    _compare_slices(oracle_lib, w, inp, got, [(0, 0), (0, 1)], True)
+
+
 # ---------------------------------------------------------------------------
 # Invariants at full size (no oracle)
 # ---------------------------------------------------------------------------
