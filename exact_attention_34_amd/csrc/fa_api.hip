@@ -228,6 +228,13 @@ int fa_fwd_splitkv(int dtype, int B, int H, int N, int d, const void *Q, const v
   if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O) || !vec_ok(LSE) ||
       !tensor_ok(workspace))
     return FA_ERR_INVALID_ARG;
+  if (N > 1 && resolve_split(B, H, N, N, nsplit) == 1) {
+    // One range: the plain forward computes the same rows without the fp32
+    // round trip through the workspace and the merge.
+    if (workspace_bytes < split_bytes(1, B, H, N, d)) return FA_ERR_WORKSPACE;
+    return status(fa::launch_fwd(dtype, B, H, N, d, Q, K, V, scale, causal, O, LSE,
+                                 (hipStream_t)stream));
+  }
   return run_split(dtype, B, H, N, N, d, Q, K, V, scale, causal, nsplit, O, LSE, workspace,
                    workspace_bytes, stream);
 }

@@ -111,7 +111,9 @@ int fa_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
  * workspace: at least fa_fwd_splitkv_workspace_bytes(...) bytes, 256-byte
  *   aligned, caller-owned, overwritten: the parts' O [parts, B, H, N, d] and
  *   LSE [parts, B, H, N] in fp32.
- * Enqueues two kernels (the ranges, then the merge). Deterministic.
+ * Enqueues two kernels (the ranges, then the merge), or, when the keys form a
+ * single range and N > 1, the kernel of fa_fwd alone (same results as
+ * fa_fwd; the workspace must still be of the stated size). Deterministic.
  */
 int fa_fwd_splitkv(int dtype, int B, int H, int N, int d, const void *Q,
                    const void *K, const void *V, float scale, int causal,
