@@ -118,9 +118,9 @@ int run_split(int dtype, int B, int H, int Nq, int Nk, int d, const void *Q, con
   float *Op = (float *)workspace;
   float *Lp = (float *)((char *)workspace + split_o_bytes(parts, B, H, Nq, d));
   hipStream_t st = (hipStream_t)stream;
-  // One query per slice over one key range: the decoding kernel writes O and
-  // LSE itself (the merge of a single part would only copy them).
-  const bool direct = Nq == 1 && parts == 1;
+  // A single key range: the kernel writes O and LSE itself (the merge of a
+  // single part would only copy them).
+  const bool direct = parts == 1;
   int rc = status(fa::launch_fwd_split(dtype, B, H, Nq, Nk, d, Q, K, V, scale, causal, req, Op,
                                        Lp, direct ? O : nullptr, direct ? LSE : nullptr, st));
   if (rc != FA_OK || direct) return rc;

@@ -503,6 +503,22 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void
                                 Nq, Nk, qoff, bh, qb, kfirst, klim, c2, K0, K1, V0, V1);
 }
 
+// The same queries over a single key range (all Nk keys): the block writes O
+// and LSE itself, as the plain forward does, so no merge is needed.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(FwdCfg<D>::kThreads, FwdCfg<D>::kWavesPerSimd) void fwd_kv_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int Nq,
+    int Nk, int qoff, int nqb, int total, float c2) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[C::TILE], K1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[C::TILE], V1[C::TILE];
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int bh = tile / nqb, qb = tile - bh * nqb;
+  fwd_block<T, D, 4, CAUSAL, false>(Q, K, V, O, LSE, nullptr, nullptr, Nq, Nk, qoff, bh, qb, 0,
+                                    Nk, c2, K0, K1, V0, V1);
+}
+
 // Merge of partial results over disjoint key sets, per row r and part s:
 //   LSE_r = log sum_s exp(LSE_sr),  O_r = sum_s exp(LSE_sr - LSE_r) O_sr,
 // the closed form of folding the two-block merge of (m, l, O~) ("Flash
@@ -869,12 +885,21 @@ struct SplitArgs {
   float c2;
   float *Op, *Lp;
   int nsplit, split_keys;
+  void *O;     // single range: final O and LSE instead of the parts
+  float *LSE;
 };
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t fwd_split(const SplitArgs &a, hipStream_t st) {
   using C = FwdCfg<D>;
   const int nqb = (a.Nq + C::BR - 1) / C::BR;
+  if (a.O != nullptr) {  // a single range, final output
+    const int total = a.BH * nqb;
+    hipLaunchKernelGGL((fwd_kv_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
+                       (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                       (uint16_t *)a.O, a.LSE, a.Nq, a.Nk, a.qoff, nqb, total, a.c2);
+    return hipGetLastError();
+  }
   const int total = a.BH * a.nsplit * nqb;
   hipLaunchKernelGGL((fwd_split_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
                      (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V, a.Op,
@@ -891,7 +916,7 @@ hipError_t launch_fwd_split(int dtype, int B, int H, int Nq, int Nk, int d, cons
                             const void *K, const void *V, float scale, int causal, int nsplit,
                             float *Op, float *Lp, void *O, float *LSE, hipStream_t st) {
   const SplitArgs a{B * H, Nq, Nk, causal ? Nk - Nq : 0, Q, K, V, scale * kLog2e, Op, Lp,
-                    split_parts(Nk, nsplit), split_key_count(Nk, nsplit)};
+                    split_parts(Nk, nsplit), split_key_count(Nk, nsplit), O, LSE};
   if (Nq == 1) {
     // One query per slice (it sees every key, masked or not): the vector
     // kernel, one workgroup per slice and key range.

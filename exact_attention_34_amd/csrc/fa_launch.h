@@ -39,9 +39,9 @@ inline int split_parts(int N, int nsplit) {
 
 // Partial results of every range of the Nk keys for Nq queries (query i at
 // position Nk - Nq + i under the causal mask): O parts fp32
-// [parts, B*H*Nq, d] at Op, LSE parts fp32 [parts, B*H*Nq] at Lp. With
-// Nq = 1 and a single range, O (dtype) and LSE may be given instead: the
-// decoding kernel then writes the final result and no merge is needed.
+// [parts, B*H*Nq, d] at Op, LSE parts fp32 [parts, B*H*Nq] at Lp. With a
+// single range, O (dtype) and LSE may be given instead: the kernel then
+// writes the final result and no merge is needed.
 hipError_t launch_fwd_split(int dtype, int B, int H, int Nq, int Nk, int d, const void *Q,
                             const void *K, const void *V, float scale, int causal, int nsplit,
                             float *Op, float *Lp, void *O, float *LSE, hipStream_t stream);
