@@ -176,6 +176,16 @@ def test_splitkv_parts_and_workspace(L, N, nsplit, parts):
     assert L.fa_fwd_splitkv_parts(2, 3, N, -1) == 0
 
 
+@pytest.mark.parametrize("B,H,Nk,parts", [(16, 32, 8192, 1), (1, 32, 32768, 8), (4, 8, 65536, 8),
+                                           (8, 8, 8192, 4), (1, 1, 300, 1), (1, 1, 100000, 63)])
+def test_decoding_split_choice(L, B, H, Nk, parts):
+    """Decoding (Nq = 1) with nsplit = 0: about one workgroup per compute unit
+    (256 without a device), ranges of at least 256 keys, at most 64 requested
+    (whole 64-key tiles divided evenly: 100000 keys in 64 requested ranges
+    make 63 of 25 tiles)."""
+    assert L.fa_fwd_kvcache_parts(B, H, 1, Nk, 0) == parts
+
+
 def test_lse_merge_rejects(L):
     m = lambda dtype=0, parts=2, rows=10, d=64, op=A, lp=A, o=A2, lse=A2: L.fa_lse_merge(
         dtype, parts, rows, d, op, lp, o, lse, None)
