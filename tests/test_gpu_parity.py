@@ -140,6 +140,29 @@ def test_c4_forward_rows_more_slices(fa, oracle_lib):
                   l_ref, what="c4 head %d" % h)
 
 
+@pytest.mark.parametrize("name", ["perf-8k", "perf-8k-causal"])
+def test_headline_shape(fa, oracle_lib, name):
+    """The N = 8192 throughput shape (B2 H16 d128 bf16) in the launch
+    configuration the benchmark times: one slice's forward and backward in
+    full against the oracle, and 16 forward rows from every other slice."""
+    w = ai.WORKLOADS[name]
+    inp = ai.make_inputs(w)
+    got = _run(fa, w, inp)
+    _compare_slices(oracle_lib, w, inp, got, [(1, 7)], True)
+    rng = np.random.default_rng(8)
+    for b in range(w.B):
+        for h in range(w.H):
+            if (b, h) == (1, 7):
+                continue
+            rows = np.sort(rng.choice(w.N, 16, replace=False))
+            rows[0], rows[-1] = 0, w.N - 1
+            k, v = f64(inp["k"][b, h]), f64(inp["v"][b, h])
+            o_ref, l_ref = oracle_lib.attention_fwd_rows(f64(inp["q"][b, h])[rows], rows, k, v,
+                                                         w.scale, w.causal)
+            check_fwd(w.dtype, f64(got["o"][b, h])[rows], f64(got["lse"][b, h])[rows], o_ref,
+                      l_ref, what="%s slice %d,%d" % (name, b, h))
+
+
 @pytest.mark.parametrize("causal,N", [(False, 4000), (True, 4500)])
 def test_eight_wave_blocks_ragged(fa, oracle_lib, causal, N):
     """Shapes on which the forward and the dQ sweep run 256-row workgroups
