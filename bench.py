@@ -32,7 +32,7 @@ Prints ONE JSON line. Besides the required keys it carries:
                 8192-key cache; HBM-bound, reported in GB/s of K and V read)
                 and chunked prefill (512 new queries over 8192 keys).
   gpu_clock     graphics clock (mean over the XCDs) and socket power sampled
-                with amd-smi while the main workload runs (settle, timed and
+                with amdsmi (in-process) while the main workload runs (settle, timed and
                 forward-only launches, after the first 0.8 s), and the dense
                 bf16 MFMA rate at that clock.
   kernels       each kernel of the step: mean launch time (HIP events), the
@@ -43,7 +43,6 @@ import argparse
 import hashlib
 import json
 import os
-import subprocess
 import sys
 import threading
 import time
@@ -119,52 +118,91 @@ def _step_fns(fa, torch, w, d):
 
 
 class ClockSampler:
-    """Samples GPU 0's graphics clocks and socket power with amd-smi in a
-    background thread (a child process per sample; nothing touches the GPU
-    from here). Samples from the first `skip_s` seconds are dropped: the
-    clock is still climbing from idle then."""
+    """Samples the GPU's graphics clocks (mean over the XCDs) and socket power
+    in a background thread, through the amdsmi library loaded in this process
+    (sysfs reads through the kernel driver: no HIP call, no child process).
+    Samples from the first `skip_s` seconds are dropped: the clock is still
+    climbing from idle then. It does not start under a profiler's preloaded
+    library (reported as an error in the result instead)."""
 
-    CMD = ["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"]
+    TOOL = "amdsmi (in-process): gpu_metrics current_gfxclks, current_socket_power"
 
     def __init__(self, period_s=0.2, skip_s=0.8):
         self.period_s, self.skip_s = period_s, skip_s
         self.samples, self.error = [], None
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
+        self._smi, self._handle = None, None
 
     @staticmethod
-    def _parse(text):
-        starts = [i for i in (text.find("{"), text.find("[")) if i >= 0]
-        data = json.loads(text[min(starts):] if starts else text)
-        if isinstance(data, dict):
-            data = data.get("gpu_data", [data])
-        g = data[0]
-        clks = [v["clk"]["value"] for k, v in g["clock"].items()
-                if k.startswith("gfx_") and isinstance(v, dict)
-                and isinstance(v.get("clk", {}).get("value"), (int, float))]
-        pw = g.get("power", {}).get("socket_power", {}).get("value")
+    def profiler_present():
+        pre = os.environ.get("LD_PRELOAD", "")
+        return "rocprof" in pre or any(k.startswith(("ROCPROF", "ROCP_")) for k in os.environ)
+
+    @staticmethod
+    def _num(x):
+        return x if isinstance(x, (int, float)) and not isinstance(x, bool) else None
+
+    def _open(self):
+        import amdsmi
+        amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if not handles:
+            raise RuntimeError("amdsmi sees no GPU")
+        handle = handles[0]
+        if len(handles) > 1:
+            # Several GPUs visible to amdsmi: take the one torch runs on, by
+            # PCI bus.
+            import torch
+            pr = torch.cuda.get_device_properties(torch.cuda.current_device())
+            bus = getattr(pr, "pci_bus_id", None)
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)   # "dddd:bb:dd.f"
+                if bus is not None and int(bdf.split(":")[1], 16) == bus:
+                    handle = h
+                    break
+        self._smi, self._handle = amdsmi, handle
+
+    def _sample(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = [c for c in (self._num(v) for v in (m.get("current_gfxclks") or []))
+                if c is not None and 0 < c < 10000]
+        if not clks and self._num(m.get("current_gfxclk")):
+            clks = [m["current_gfxclk"]]
+        pw = self._num(m.get("current_socket_power"))
+        if pw is None or pw >= 0xFFFF:
+            pw = self._num(m.get("average_socket_power"))
         return (sum(clks) / len(clks) if clks else None,
-                pw if isinstance(pw, (int, float)) else None)
+                pw if pw is not None and pw < 0xFFFF else None)
 
     def _run(self):
         t0 = time.perf_counter()
-        while not self._stop.is_set():
-            try:
-                r = subprocess.run(self.CMD, capture_output=True, text=True, timeout=5)
-                clk, pw = self._parse(r.stdout)
+        try:
+            self._open()
+            while not self._stop.is_set():
+                clk, pw = self._sample()
                 if time.perf_counter() - t0 >= self.skip_s and clk is not None:
                     self.samples.append((clk, pw))
-            except Exception as e:  # no amd-smi, or output it cannot parse
-                self.error = "%s: %s" % (type(e).__name__, e)
-                return
-            self._stop.wait(self.period_s)
+                self._stop.wait(self.period_s)
+        except Exception as e:  # no amdsmi, no permission, or fields it lacks
+            self.error = "%s: %s" % (type(e).__name__, e)
+        finally:
+            if self._smi is not None:
+                try:
+                    self._smi.amdsmi_shut_down()
+                except Exception:
+                    pass
 
     def start(self):
+        if self.profiler_present():
+            self.error = "not sampled under a profiler"
+            return
         self._thread.start()
 
     def stop(self):
         self._stop.set()
-        self._thread.join(timeout=10)
+        if self._thread.is_alive():
+            self._thread.join(timeout=10)
         if not self.samples:
             return {"samples": 0, "error": self.error or "no sample"}
         clk = sorted(c for c, _ in self.samples)
@@ -174,7 +212,7 @@ class ClockSampler:
         return {"gfx_mhz": round(med, 1), "gfx_mhz_min": round(clk[0], 1),
                 "gfx_mhz_max": round(clk[-1], 1),
                 "socket_power_w": pw[len(pw) // 2] if pw else None,
-                "samples": len(clk), "tool": " ".join(self.CMD),
+                "samples": len(clk), "tool": self.TOOL,
                 "mfma_bf16_tflops_at_clock": round(256 * 4 * 1024 * med * 1e6 / 1e12, 1)}
 
 
@@ -312,8 +350,8 @@ def splitkv_report(fa, torch, settle_s):
         d = {k: v.cuda() for k, v in ai.make_inputs(w, with_do=False).items()}
         B, H, N, D = w.B, w.H, w.N, w.d
         code = {torch.bfloat16: fa.BF16, torch.float16: fa.F16}[d["q"].dtype]
-        parts = fa.fwd_splitkv_parts(B, H, N, 0)
-        nbytes = fa.fwd_splitkv_workspace_bytes(d["q"].dtype, B, H, N, D, 0)
+        parts = fa.fwd_splitkv_parts(B, H, N, 0, w.causal)
+        nbytes = fa.fwd_splitkv_workspace_bytes(d["q"].dtype, B, H, N, D, 0, w.causal)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         o = torch.empty_like(d["q"])
         lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
@@ -360,8 +398,9 @@ def kvcache_report(fa, torch, settle_s):
         g = torch.Generator().manual_seed(42)
         q, k, v = (torch.randn(B, H, n, d, generator=g).to(torch.bfloat16).cuda()
                    for n in (Nq, Nk, Nk))
-        parts = fa.fwd_kvcache_parts(B, H, Nq, Nk, 0)
-        ws = torch.empty(fa.fwd_kvcache_workspace_bytes(torch.bfloat16, B, H, Nq, Nk, d, 0),
+        parts = fa.fwd_kvcache_parts(B, H, Nq, Nk, 0, causal)
+        ws = torch.empty(fa.fwd_kvcache_workspace_bytes(torch.bfloat16, B, H, Nq, Nk, d, 0,
+                                                        causal),
                          dtype=torch.uint8, device="cuda")
         ms = _time_ms(torch, lambda: fa.fwd_kvcache(q, k, v, d ** -0.5, causal, 0, ws), 20,
                       settle_s)
@@ -465,8 +504,8 @@ def main():
     ap.add_argument("--no-std", action="store_true",
                     help="skip the stored-P standard-attention comparison")
     ap.add_argument("--no-clock", action="store_true",
-                    help="do not sample the clock with amd-smi (under a profiler, whose "
-                         "preloaded library would start the GPU in every child process)")
+                    help="do not sample the clock and power (the sampler also stays off "
+                         "by itself under a profiler's preloaded library)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales the HBM "
                          "byte counters read under rocprofv3)")

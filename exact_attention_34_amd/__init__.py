@@ -54,15 +54,15 @@ def lib():
     L.fa_fwd.restype = i
     L.fa_fwd_splitkv.argtypes = [i, i, i, i, i, p, p, p, f, i, i, p, p, p, z, p]
     L.fa_fwd_splitkv.restype = i
-    L.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.fa_fwd_splitkv_workspace_bytes.restype = z
-    L.fa_fwd_splitkv_parts.argtypes = [i, i, i, i]
+    L.fa_fwd_splitkv_parts.argtypes = [i, i, i, i, i]
     L.fa_fwd_splitkv_parts.restype = i
     L.fa_fwd_kvcache.argtypes = [i, i, i, i, i, i, p, p, p, f, i, i, p, p, p, z, p]
     L.fa_fwd_kvcache.restype = i
-    L.fa_fwd_kvcache_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.fa_fwd_kvcache_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
     L.fa_fwd_kvcache_workspace_bytes.restype = z
-    L.fa_fwd_kvcache_parts.argtypes = [i, i, i, i, i]
+    L.fa_fwd_kvcache_parts.argtypes = [i, i, i, i, i, i]
     L.fa_fwd_kvcache_parts.restype = i
     L.fa_lse_merge.argtypes = [i, i, ctypes.c_longlong, i, p, p, p, p, p]
     L.fa_lse_merge.restype = i
@@ -111,6 +111,28 @@ def _check_qkv(*ts):
     return (_CODES[t0.dtype],) + tuple(t0.shape)
 
 
+def _check_rows(t, name, ref):
+    """A per-row fp32 vector (LSE or D) that the kernels index as [B, H, N]
+    on ref's device: anything else would be read or written out of bounds."""
+    B, H, N = ref.shape[:3]
+    if (not isinstance(t, torch.Tensor) or t.shape != (B, H, N) or t.dtype != torch.float32
+            or t.device != ref.device or not t.is_contiguous()):
+        raise ValueError("%s must be a contiguous fp32 [B, H, N] tensor on %s"
+                         % (name, ref.device))
+
+
+def _workspace(ws, nbytes, ref):
+    """The caller's workspace (device memory on ref's device, contiguous, at
+    least nbytes) or a new one."""
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=ref.device)
+    if (not isinstance(ws, torch.Tensor) or ws.device != ref.device or not ws.is_contiguous()
+            or ws.numel() * ws.element_size() < nbytes):
+        raise ValueError("workspace must be a contiguous tensor of at least %d bytes on %s"
+                         % (nbytes, ref.device))
+    return ws
+
+
 def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
@@ -135,22 +157,22 @@ def fwd(q, k, v, scale=None, causal=False):
     return o, lse
 
 
-def fwd_splitkv_workspace_bytes(dtype, B, H, N, d, nsplit=0):
-    return int(lib().fa_fwd_splitkv_workspace_bytes(_CODES[dtype], B, H, N, d, int(nsplit)))
+def fwd_splitkv_workspace_bytes(dtype, B, H, N, d, nsplit=0, causal=False):
+    return int(lib().fa_fwd_splitkv_workspace_bytes(_CODES[dtype], B, H, N, d, int(nsplit),
+                                                   int(bool(causal))))
 
 
-def fwd_splitkv_parts(B, H, N, nsplit=0):
+def fwd_splitkv_parts(B, H, N, nsplit=0, causal=False):
     """Key ranges fwd_splitkv uses for this nsplit (0: the library's choice)."""
-    return int(lib().fa_fwd_splitkv_parts(B, H, N, int(nsplit)))
+    return int(lib().fa_fwd_splitkv_parts(B, H, N, int(nsplit), int(bool(causal))))
 
 
 def fwd_splitkv(q, k, v, scale=None, causal=False, nsplit=0, workspace=None):
     """O, LSE as fwd(), with each row's keys split into ranges swept by separate
     workgroups and the partial results merged (nsplit=0: the library picks)."""
     dt, B, H, N, d = _check_qkv(q, k, v)
-    nbytes = fwd_splitkv_workspace_bytes(q.dtype, B, H, N, d, nsplit)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    nbytes = fwd_splitkv_workspace_bytes(q.dtype, B, H, N, d, nsplit, causal)
+    workspace = _workspace(workspace, nbytes, q)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _call("fa_fwd_splitkv", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _scale(scale, d),
@@ -159,30 +181,31 @@ def fwd_splitkv(q, k, v, scale=None, causal=False, nsplit=0, workspace=None):
     return o, lse
 
 
-def fwd_kvcache_workspace_bytes(dtype, B, H, Nq, Nk, d, nsplit=0):
+def fwd_kvcache_workspace_bytes(dtype, B, H, Nq, Nk, d, nsplit=0, causal=True):
     return int(lib().fa_fwd_kvcache_workspace_bytes(_CODES[dtype], B, H, Nq, Nk, d,
-                                                   int(nsplit)))
+                                                   int(nsplit), int(bool(causal))))
 
 
-def fwd_kvcache_parts(B, H, Nq, Nk, nsplit=0):
-    return int(lib().fa_fwd_kvcache_parts(B, H, Nq, Nk, int(nsplit)))
+def fwd_kvcache_parts(B, H, Nq, Nk, nsplit=0, causal=True):
+    return int(lib().fa_fwd_kvcache_parts(B, H, Nq, Nk, int(nsplit), int(bool(causal))))
 
 
 def fwd_kvcache(q, k, v, scale=None, causal=True, nsplit=0, workspace=None):
     """O, LSE of Nq new queries ([B, H, Nq, d]) over Nk cached keys and values
     ([B, H, Nk, d]); under the causal mask query i sits at position Nk-Nq+i."""
     for t in (q, k, v):
-        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError("expected contiguous GPU tensors [B, H, n, d] of one dtype")
+        if (t.dim() != 4 or not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype
+                or t.device != q.device):
+            raise ValueError("expected contiguous GPU tensors [B, H, n, d] of one dtype "
+                             "on one device")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     if k.shape != (B, H, Nk, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B, H, Nk, d]")
     if q.dtype not in _CODES:
         raise ValueError("unsupported dtype %s" % q.dtype)
-    nbytes = fwd_kvcache_workspace_bytes(q.dtype, B, H, Nq, Nk, d, nsplit)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    nbytes = fwd_kvcache_workspace_bytes(q.dtype, B, H, Nq, Nk, d, nsplit, causal)
+    workspace = _workspace(workspace, nbytes, q)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     _call("fa_fwd_kvcache", _CODES[q.dtype], B, H, Nq, Nk, d, _ptr(q), _ptr(k), _ptr(v),
@@ -199,8 +222,11 @@ def lse_merge(o_parts, lse_parts, out_dtype=torch.float32):
     if o_parts.dim() != 3 or lse_parts.shape != o_parts.shape[:2]:
         raise ValueError("expected o_parts [P, rows, d] and lse_parts [P, rows]")
     for t in (o_parts, lse_parts):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("parts must be contiguous fp32 GPU tensors")
+        if (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()
+                or t.device != o_parts.device):
+            raise ValueError("parts must be contiguous fp32 GPU tensors on one device")
+    if out_dtype not in _CODES:
+        raise ValueError("unsupported dtype %s" % out_dtype)
     P, rows, d = o_parts.shape
     o = torch.empty((rows, d), dtype=out_dtype, device=o_parts.device)
     lse = torch.empty(rows, dtype=torch.float32, device=o_parts.device)
@@ -216,11 +242,9 @@ def bwd_workspace_bytes(dtype, B, H, N, d):
 def bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None):
     """dQ, dK, dV of attention given dO, and O, LSE from fwd()."""
     dt, B, H, N, d = _check_qkv(q, k, v, o, do)
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    _check_rows(lse, "lse", q)
     nbytes = bwd_workspace_bytes(q.dtype, B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, nbytes, q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     _call("fa_bwd", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
           _ptr(lse), _scale(scale, d), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -231,12 +255,15 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None):
 def bwd_preprocess(o, do, dvec):
     """Stage 1 of bwd: dvec = rowsum(dO o O), fp32 [B, H, N]."""
     dt, B, H, N, d = _check_qkv(o, do)
+    _check_rows(dvec, "dvec", o)
     _call("fa_bwd_preprocess", dt, B, H, N, d, _ptr(o), _ptr(do), _ptr(dvec), _stream(o))
 
 
 def bwd_dkdv(q, k, v, do, lse, dvec, dk, dv, scale=None, causal=False):
     """Stage 2 of bwd: dK and dV (key blocks outer)."""
     dt, B, H, N, d = _check_qkv(q, k, v, do, dk, dv)
+    _check_rows(lse, "lse", q)
+    _check_rows(dvec, "dvec", q)
     _call("fa_bwd_dkdv", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
           _ptr(dvec), _scale(scale, d), int(bool(causal)), _ptr(dk), _ptr(dv), _stream(q))
 
@@ -245,6 +272,8 @@ def bwd_dq_d(q, k, v, o, do, lse, dvec, dq, scale=None, causal=False):
     """Stage 3 with stage 1 folded in: dQ, and dvec = rowsum(dO o O) written
     for a bwd_dkdv that follows."""
     dt, B, H, N, d = _check_qkv(q, k, v, o, do, dq)
+    _check_rows(lse, "lse", q)
+    _check_rows(dvec, "dvec", q)
     _call("fa_bwd_dq_d", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
           _ptr(lse), _ptr(dvec), _scale(scale, d), int(bool(causal)), _ptr(dq), _stream(q))
 
@@ -252,6 +281,8 @@ def bwd_dq_d(q, k, v, o, do, lse, dvec, dq, scale=None, causal=False):
 def bwd_dq(q, k, v, do, lse, dvec, dq, scale=None, causal=False):
     """Stage 3 of bwd: dQ (query blocks outer)."""
     dt, B, H, N, d = _check_qkv(q, k, v, do, dq)
+    _check_rows(lse, "lse", q)
+    _check_rows(dvec, "dvec", q)
     _call("fa_bwd_dq", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
           _ptr(dvec), _scale(scale, d), int(bool(causal)), _ptr(dq), _stream(q))
 
@@ -280,9 +311,7 @@ def std_fwd(q, k, v, scale=None, causal=False, workspace=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     P = torch.empty((B, H, N, std_row_stride(N)), dtype=q.dtype, device=q.device)
-    if workspace is None:
-        workspace = torch.empty(std_fwd_workspace_bytes(q.dtype, B, H, N, d), dtype=torch.uint8,
-                                device=q.device)
+    workspace = _workspace(workspace, std_fwd_workspace_bytes(q.dtype, B, H, N, d), q)
     _call("fa_std_fwd", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _scale(scale, d),
           int(bool(causal)), _ptr(o), _ptr(lse), _ptr(P), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _stream(q))
@@ -292,11 +321,10 @@ def std_fwd(q, k, v, scale=None, causal=False, workspace=None):
 def std_bwd(q, k, v, o, do, P, scale=None, workspace=None):
     """dQ, dK, dV of the standard path from the stored P of std_fwd()."""
     dt, B, H, N, d = _check_qkv(q, k, v, o, do)
-    if P.shape != (B, H, N, std_row_stride(N)) or P.dtype != q.dtype or not P.is_contiguous():
+    if (P.shape != (B, H, N, std_row_stride(N)) or P.dtype != q.dtype or not P.is_contiguous()
+            or P.device != q.device):
         raise ValueError("P must be std_fwd's [B, H, N, row stride] array")
-    if workspace is None:
-        workspace = torch.empty(std_bwd_workspace_bytes(q.dtype, B, H, N, d), dtype=torch.uint8,
-                                device=q.device)
+    workspace = _workspace(workspace, std_bwd_workspace_bytes(q.dtype, B, H, N, d), q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     _call("fa_std_bwd", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(P),
           _scale(scale, d), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),

@@ -46,29 +46,43 @@ size_t d_bytes(int B, int H, int N) { return round_up((size_t)B * H * N * sizeof
 
 constexpr int kMaxSplit = 64;
 
-// Key ranges for fa_fwd_splitkv when the caller passes 0: enough workgroups
-// (one per slice, range and 128-row query block) to give every compute unit
-// two, with at least 16 key tiles per range (shorter ranges do not repay the
-// extra kernel and the merge: at B2 H8 N1024 two ranges of 8 tiles ran
-// 0.017 ms and four of 4 tiles 0.022 ms, against 0.015 ms unsplit).
-int auto_split(int B, int H, int Nq, int Nk) {
+// Key ranges for fa_fwd_splitkv / fa_fwd_kvcache when the caller passes 0,
+// from the number of workgroups the unsplit launch would run against the
+// compute-unit count; ranges keep at least 16 key tiles (shorter ranges do
+// not repay the extra kernel and the merge: at B2 H8 N1024 two ranges of 8
+// tiles ran 0.017 ms and four of 4 tiles 0.022 ms, against 0.015 ms unsplit).
+//  * Nq = Nk (self-attention; one range runs the plain forward): that
+//    forward's units, 128-row blocks, paired under the causal mask. Split
+//    only below one unit per compute unit: at B1 H4 N8192 d128 non-causal
+//    (256 units) two ranges ran 0.132 ms (merge included) against 0.128 ms
+//    unsplit; causal (128 pair units) 0.100 against 0.114 ms.
+//  * Nq != Nk (new queries over a cache): the split kernel's units (one per
+//    slice, range and 128-row block), about two per compute unit (prefill of
+//    512 queries over 8192 keys, 32 slices: four ranges, 0.075 ms).
+//  * Nq = 1 (decoding, vector kernel, HBM-bound): about one workgroup of
+//    four waves per compute unit, ranges of at least 256 keys. Measured at
+//    d = 128 over 1 to 64 ranges: K/V read rates peak (5.1-6.0 TB/s) at
+//    256-512 workgroups and fall with more (B1 H32 Nk32768: 8 ranges
+//    5.10 TB/s, 32 ranges 4.34; B16 H32 Nk8192: 1 range 5.84, 16 ranges 5.66).
+int auto_split(int B, int H, int Nq, int Nk, int causal) {
   int cus = 256, dev = 0, v = 0;
   if (hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
     cus = v;
+  const long bh = (long)B * H;
   long ns;
   if (Nq == 1) {
-    // Decoding (vector kernel, HBM-bound): about one workgroup of four waves
-    // per compute unit, ranges of at least 256 keys. Measured at d = 128 over
-    // 1 to 64 ranges: K/V read rates peak (5.1-6.0 TB/s) at 256-512
-    // workgroups and fall with more (B1 H32 Nk32768: 8 ranges 5.10 TB/s,
-    // 32 ranges 4.34; B16 H32 Nk8192: 1 range 5.84, 16 ranges 5.66).
-    const long bh = (long)B * H;
     ns = (cus + bh - 1) / bh;
     if (ns > Nk / 256) ns = Nk / 256;
   } else {
-    const long units = (long)B * H * ((Nq + 127) / 128);
-    ns = (2L * cus + units - 1) / units;
+    const long nqb = (Nq + 127) / 128;
+    if (Nq == Nk) {
+      const long units = bh * (causal ? (nqb + 1) / 2 : nqb);
+      ns = (cus + units - 1) / units;
+    } else {
+      const long units = bh * nqb;
+      ns = (2L * cus + units - 1) / units;
+    }
     const long tiles = (Nk + 63) / 64;
     if (ns > tiles / 16) ns = tiles / 16;
   }
@@ -77,9 +91,9 @@ int auto_split(int B, int H, int Nq, int Nk) {
 }
 
 // Requested split count -> ranges actually used (0 if invalid).
-int resolve_split(int B, int H, int Nq, int Nk, int nsplit) {
+int resolve_split(int B, int H, int Nq, int Nk, int nsplit, int causal) {
   if (nsplit < 0 || nsplit > kMaxSplit) return 0;
-  if (nsplit == 0) nsplit = auto_split(B, H, Nq, Nk);
+  if (nsplit == 0) nsplit = auto_split(B, H, Nq, Nk, causal);
   return fa::split_parts(Nk, nsplit);
 }
 
@@ -109,7 +123,7 @@ int run_split(int dtype, int B, int H, int Nq, int Nk, int d, const void *Q, con
               const void *V, float scale, int causal, int nsplit, void *O, float *LSE,
               void *workspace, size_t workspace_bytes, void *stream) {
   if (nsplit < 0 || nsplit > kMaxSplit) return FA_ERR_INVALID_ARG;
-  const int req = nsplit == 0 ? auto_split(B, H, Nq, Nk) : nsplit;
+  const int req = nsplit == 0 ? auto_split(B, H, Nq, Nk, causal) : nsplit;
   const int parts = fa::split_parts(Nk, req);
   // One workgroup per slice, key range and 128-row query block: at most
   // B*H*Nq/2 + B*H*parts with parts <= min(64, Nk/64), below 2^31 given
@@ -167,29 +181,32 @@ int fa_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, 
                                (hipStream_t)stream));
 }
 
-size_t fa_fwd_splitkv_workspace_bytes(int dtype, int B, int H, int N, int d, int nsplit) {
+size_t fa_fwd_splitkv_workspace_bytes(int dtype, int B, int H, int N, int d, int nsplit,
+                                      int causal) {
   if (check_shape(dtype, B, H, N, d, false) != FA_OK || dtype == FA_F32) return 0;
-  const int parts = resolve_split(B, H, N, N, nsplit);
+  if (causal != 0 && causal != 1) return 0;
+  const int parts = resolve_split(B, H, N, N, nsplit, causal);
   if (parts == 0) return 0;
   return split_bytes(parts, B, H, N, d);
 }
 
-int fa_fwd_splitkv_parts(int B, int H, int N, int nsplit) {
-  if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return resolve_split(B, H, N, N, nsplit);
+int fa_fwd_splitkv_parts(int B, int H, int N, int nsplit, int causal) {
+  if (B <= 0 || H <= 0 || N <= 0 || (causal != 0 && causal != 1)) return 0;
+  return resolve_split(B, H, N, N, nsplit, causal);
 }
 
 size_t fa_fwd_kvcache_workspace_bytes(int dtype, int B, int H, int Nq, int Nk, int d,
-                                      int nsplit) {
-  if (check_kv_shape(dtype, B, H, Nq, Nk, d, 0) != FA_OK) return 0;
-  const int parts = resolve_split(B, H, Nq, Nk, nsplit);
+                                      int nsplit, int causal) {
+  if (causal != 0 && causal != 1) return 0;
+  if (check_kv_shape(dtype, B, H, Nq, Nk, d, causal) != FA_OK) return 0;
+  const int parts = resolve_split(B, H, Nq, Nk, nsplit, causal);
   if (parts == 0) return 0;
   return split_bytes(parts, B, H, Nq, d);
 }
 
-int fa_fwd_kvcache_parts(int B, int H, int Nq, int Nk, int nsplit) {
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0) return 0;
-  return resolve_split(B, H, Nq, Nk, nsplit);
+int fa_fwd_kvcache_parts(int B, int H, int Nq, int Nk, int nsplit, int causal) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (causal != 0 && causal != 1)) return 0;
+  return resolve_split(B, H, Nq, Nk, nsplit, causal);
 }
 
 int fa_fwd_kvcache(int dtype, int B, int H, int Nq, int Nk, int d, const void *Q, const void *K,
@@ -228,7 +245,7 @@ int fa_fwd_splitkv(int dtype, int B, int H, int N, int d, const void *Q, const v
   if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O) || !vec_ok(LSE) ||
       !tensor_ok(workspace))
     return FA_ERR_INVALID_ARG;
-  if (N > 1 && resolve_split(B, H, N, N, nsplit) == 1) {
+  if (N > 1 && resolve_split(B, H, N, N, nsplit, causal) == 1) {
     // One range: the plain forward computes the same rows without the fp32
     // round trip through the workspace and the merge.
     if (workspace_bytes < split_bytes(1, B, H, N, d)) return FA_ERR_WORKSPACE;

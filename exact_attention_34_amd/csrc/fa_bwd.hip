@@ -514,7 +514,9 @@ __device__ __forceinline__ void dq_block(
   auto issue = [&](int b, int kt) __attribute__((always_inline)) {
     uint16_t *Kb = kv + 2 * b * C::TILE, *Vb = Kb + C::TILE;
     const int kb = kt * C::BC;
-    const int soff = kb * D * 2;
+    // Byte offset of the tile in the slice: below N*D*2 < 2^32 (the slice
+    // limit of the interface), so it fits the unsigned 32-bit soffset.
+    const uint32_t soff = (uint32_t)kb * D * 2;
     if (kb + C::BC <= N) {
 #pragma unroll
       for (int i = 0; i < C::LPW; ++i) {

@@ -199,12 +199,12 @@ __device__ __forceinline__ void buffer_load_lds16(const i32x4 &rsrc, int voffset
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
-__device__ __forceinline__ void dma_lds16(const i32x4 &rsrc, int voffset, int soffset,
+__device__ __forceinline__ void dma_lds16(const i32x4 &rsrc, int voffset, uint32_t soffset,
                                           const void *lds_base) {
   uint32_t saved;
   // Wave-uniform by contract; kept in SGPRs (the soffset field takes no
-  // literal).
-  soffset = __builtin_amdgcn_readfirstlane(soffset);
+  // literal). An unsigned byte offset: the full 32-bit range is valid.
+  soffset = (uint32_t)__builtin_amdgcn_readfirstlane((int)soffset);
   uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
   asm("" : "+s"(soffset), "+s"(m0v));
   asm volatile(
@@ -217,12 +217,12 @@ __device__ __forceinline__ void dma_lds16(const i32x4 &rsrc, int voffset, int so
       : "s"(m0v), "v"(voffset), "s"(rsrc), "s"(soffset)
       : "memory");
 }
-__device__ __forceinline__ void dma_lds4(const i32x4 &rsrc, int voffset, int soffset,
-                                         const void *lds_base) {
+__device__ __forceinline__ void dma_lds4(const i32x4 &rsrc, int voffset, uint32_t soffset,
+                                          const void *lds_base) {
   uint32_t saved;
   // Wave-uniform by contract; kept in SGPRs (the soffset field takes no
-  // literal).
-  soffset = __builtin_amdgcn_readfirstlane(soffset);
+  // literal). An unsigned byte offset: the full 32-bit range is valid.
+  soffset = (uint32_t)__builtin_amdgcn_readfirstlane((int)soffset);
   uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
   asm("" : "+s"(soffset), "+s"(m0v));
   asm volatile(

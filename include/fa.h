@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 /* element types */
 #define FA_F32 0
@@ -105,8 +105,10 @@ int fa_fwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
  *
  * nsplit: 1..64 ranges at most (the key tiles of 64 keys are divided evenly
  *   and no range is empty, so fewer may be used: fa_fwd_splitkv_parts), or 0
- *   to let the library choose from the grid size and the current device's
- *   compute-unit count.
+ *   to let the library choose from the grid size (which depends on causal:
+ *   the unsplit causal forward pairs its query blocks) and the current
+ *   device's compute-unit count; keys are split only where the unsplit
+ *   forward would leave compute units idle.
  * In/Out: as fa_fwd. dtype FA_F16 or FA_BF16 (FA_F32: FA_ERR_UNSUPPORTED).
  * workspace: at least fa_fwd_splitkv_workspace_bytes(...) bytes, 256-byte
  *   aligned, caller-owned, overwritten: the parts' O [parts, B, H, N, d] and
@@ -120,12 +122,14 @@ int fa_fwd_splitkv(int dtype, int B, int H, int N, int d, const void *Q,
                    int nsplit, void *O, float *LSE, void *workspace,
                    size_t workspace_bytes, void *stream);
 
-/* Workspace bytes fa_fwd_splitkv needs (0 for arguments it would reject). */
+/* Workspace bytes fa_fwd_splitkv needs for these arguments, the same nsplit
+ * and causal (0 for arguments it would reject). */
 size_t fa_fwd_splitkv_workspace_bytes(int dtype, int B, int H, int N, int d,
-                                      int nsplit);
+                                      int nsplit, int causal);
 
-/* Number of key ranges fa_fwd_splitkv uses for this nsplit (0 if invalid). */
-int fa_fwd_splitkv_parts(int B, int H, int N, int nsplit);
+/* Number of key ranges fa_fwd_splitkv uses for this nsplit and causal (0 if
+ * invalid). */
+int fa_fwd_splitkv_parts(int B, int H, int N, int nsplit, int causal);
 
 /*
  * Forward of Nq new queries over Nk keys, for streaming use of the online
@@ -146,12 +150,15 @@ int fa_fwd_kvcache(int dtype, int B, int H, int Nq, int Nk, int d,
                    int causal, int nsplit, void *O, float *LSE,
                    void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace bytes fa_fwd_kvcache needs (0 for arguments it would reject). */
+/* Workspace bytes fa_fwd_kvcache needs for these arguments, the same nsplit
+ * and causal (0 for arguments it would reject). */
 size_t fa_fwd_kvcache_workspace_bytes(int dtype, int B, int H, int Nq, int Nk,
-                                      int d, int nsplit);
+                                      int d, int nsplit, int causal);
 
-/* Number of key ranges fa_fwd_kvcache uses for this nsplit (0 if invalid). */
-int fa_fwd_kvcache_parts(int B, int H, int Nq, int Nk, int nsplit);
+/* Number of key ranges fa_fwd_kvcache uses for this nsplit and causal (0 if
+ * invalid). */
+int fa_fwd_kvcache_parts(int B, int H, int Nq, int Nk, int nsplit,
+                         int causal);
 
 /*
  * Merge of partial attention results over disjoint key sets ([FA] section 2,

@@ -145,7 +145,8 @@ def test_binding_fails_loudly_without_gpu_tensors():
 
 def _split(L, dtype=2, N=16, d=64, nsplit=2, ws=A, ws_bytes=None, causal=0, o=A2):
     if ws_bytes is None:
-        ws_bytes = L.fa_fwd_splitkv_workspace_bytes(dtype, 1, 1, N, d, nsplit)
+        ws_bytes = L.fa_fwd_splitkv_workspace_bytes(dtype, 1, 1, N, d, nsplit,
+                                                    causal if causal in (0, 1) else 0)
     return L.fa_fwd_splitkv(dtype, 1, 1, N, d, A, A, A, 0.125, causal, nsplit, o, A2, ws,
                             ws_bytes, None)
 
@@ -158,8 +159,9 @@ def test_splitkv_rejects(L):
     assert _split(L, causal=3) == INVALID
     assert _split(L, ws=NUL) == INVALID
     assert _split(L, o=MIS) == INVALID
-    need = L.fa_fwd_splitkv_workspace_bytes(2, 1, 1, 16, 64, 2)
+    need = L.fa_fwd_splitkv_workspace_bytes(2, 1, 1, 16, 64, 2, 0)
     assert need > 0
+    assert L.fa_fwd_splitkv_workspace_bytes(2, 1, 1, 16, 64, 2, 2) == 0
     assert _split(L, ws_bytes=need - 1) == WS
 
 
@@ -168,12 +170,30 @@ def test_splitkv_rejects(L):
 def test_splitkv_parts_and_workspace(L, N, nsplit, parts):
     """Key tiles of 64 are divided evenly over at most nsplit non-empty ranges;
     the workspace holds every part's fp32 O and LSE."""
-    assert L.fa_fwd_splitkv_parts(2, 3, N, nsplit) == parts
-    ob = -(-parts * 2 * 3 * N * 128 * 4 // 256) * 256
-    lb = -(-parts * 2 * 3 * N * 4 // 256) * 256
-    assert L.fa_fwd_splitkv_workspace_bytes(2, 2, 3, N, 128, nsplit) == ob + lb
-    assert L.fa_fwd_splitkv_workspace_bytes(0, 2, 3, N, 128, nsplit) == 0
-    assert L.fa_fwd_splitkv_parts(2, 3, N, -1) == 0
+    for causal in (0, 1):
+        assert L.fa_fwd_splitkv_parts(2, 3, N, nsplit, causal) == parts
+        ob = -(-parts * 2 * 3 * N * 128 * 4 // 256) * 256
+        lb = -(-parts * 2 * 3 * N * 4 // 256) * 256
+        assert L.fa_fwd_splitkv_workspace_bytes(2, 2, 3, N, 128, nsplit, causal) == ob + lb
+        assert L.fa_fwd_splitkv_workspace_bytes(0, 2, 3, N, 128, nsplit, causal) == 0
+        assert L.fa_fwd_splitkv_parts(2, 3, N, -1, causal) == 0
+    assert L.fa_fwd_splitkv_parts(2, 3, N, nsplit, 2) == 0
+
+
+@pytest.mark.parametrize("B,H,N,causal,parts", [
+    (1, 4, 8192, 0, 1),    # 256 query blocks: one per compute unit, no split
+    (1, 4, 8192, 1, 2),    # 128 causal pair units: two ranges
+    (1, 1, 8192, 0, 4),    # 64 blocks
+    (1, 1, 8192, 1, 8),    # 32 pair units
+    (2, 8, 1024, 0, 1),    # ranges would be shorter than 16 key tiles
+    (16, 32, 2048, 1, 1),  # thousands of units
+    (1, 2, 4096, 1, 4)])   # 32 pair units; 64 key tiles give at most 4 ranges
+def test_self_attention_split_choice(L, B, H, N, causal, parts):
+    """fa_fwd_splitkv with nsplit = 0 splits only when the unsplit forward's
+    workgroups (128-row blocks, paired under the causal mask) number fewer
+    than the compute units (256 without a device), with ranges of at least
+    16 key tiles."""
+    assert L.fa_fwd_splitkv_parts(B, H, N, 0, causal) == parts
 
 
 @pytest.mark.parametrize("B,H,Nk,parts", [(16, 32, 8192, 1), (1, 32, 32768, 8), (4, 8, 65536, 8),
@@ -183,7 +203,7 @@ def test_decoding_split_choice(L, B, H, Nk, parts):
     (256 without a device), ranges of at least 256 keys, at most 64 requested
     (whole 64-key tiles divided evenly: 100000 keys in 64 requested ranges
     make 63 of 25 tiles)."""
-    assert L.fa_fwd_kvcache_parts(B, H, 1, Nk, 0) == parts
+    assert L.fa_fwd_kvcache_parts(B, H, 1, Nk, 0, 1) == parts
 
 
 def test_lse_merge_rejects(L):
@@ -209,20 +229,24 @@ def test_kvcache_rejects(L):
     assert k(nsplit=65) == INVALID
     assert k(ws=NUL) == INVALID and k(o=MIS) == INVALID
     assert k(nb=16) == WS
-    assert L.fa_fwd_kvcache_workspace_bytes(2, 1, 2, 4, 100, 64, 2) > 0
-    assert L.fa_fwd_kvcache_workspace_bytes(0, 1, 2, 4, 100, 64, 2) == 0
-    # Nq > Nk is allowed without the mask (every query sees every key)
-    assert L.fa_fwd_kvcache_workspace_bytes(2, 1, 2, 300, 100, 64, 2) > 0
+    assert L.fa_fwd_kvcache_workspace_bytes(2, 1, 2, 4, 100, 64, 2, 1) > 0
+    assert L.fa_fwd_kvcache_workspace_bytes(0, 1, 2, 4, 100, 64, 2, 1) == 0
+    # Nq > Nk is allowed without the mask (every query sees every key), not
+    # with it
+    assert L.fa_fwd_kvcache_workspace_bytes(2, 1, 2, 300, 100, 64, 2, 0) > 0
+    assert L.fa_fwd_kvcache_workspace_bytes(2, 1, 2, 300, 100, 64, 2, 1) == 0
+    assert L.fa_fwd_kvcache_parts(1, 2, 4, 100, 2, 3) == 0
 
 
 @pytest.mark.parametrize("Nq,Nk,nsplit,parts", [(1, 8192, 8, 8), (7, 100, 4, 2), (512, 8192, 3, 3)])
 def test_kvcache_parts_and_workspace(L, Nq, Nk, nsplit, parts):
     """Ranges are cut from the Nk keys; the workspace holds fp32 O and LSE for
     the Nq query rows of every part."""
-    assert L.fa_fwd_kvcache_parts(2, 3, Nq, Nk, nsplit) == parts
-    ob = -(-parts * 6 * Nq * 128 * 4 // 256) * 256
-    lb = -(-parts * 6 * Nq * 4 // 256) * 256
-    assert L.fa_fwd_kvcache_workspace_bytes(2, 2, 3, Nq, Nk, 128, nsplit) == ob + lb
+    for causal in (0, 1):
+        assert L.fa_fwd_kvcache_parts(2, 3, Nq, Nk, nsplit, causal) == parts
+        ob = -(-parts * 6 * Nq * 128 * 4 // 256) * 256
+        lb = -(-parts * 6 * Nq * 4 // 256) * 256
+        assert L.fa_fwd_kvcache_workspace_bytes(2, 2, 3, Nq, Nk, 128, nsplit, causal) == ob + lb
 
 
 # ---------------------------------------------------------------------------

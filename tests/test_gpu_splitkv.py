@@ -40,7 +40,8 @@ def test_splitkv_matches_oracle(fa, oracle_lib, dt, d, causal, N, nsplit):
     dev = {k: v.cuda() for k, v in inp.items()}
     o, lse = fa.fwd_splitkv(dev["q"], dev["k"], dev["v"], w.scale, causal, nsplit)
     torch.cuda.synchronize()
-    print(w.name, "causal", causal, "parts", fa.fwd_splitkv_parts(1, 2, N, nsplit), flush=True)
+    print(w.name, "causal", causal, "parts", fa.fwd_splitkv_parts(1, 2, N, nsplit, causal),
+          flush=True)
     for h in range(2):
         o_ref, l_ref = oracle_lib.attention_fwd(f64(inp["q"][0, h]), f64(inp["k"][0, h]),
                                                 f64(inp["v"][0, h]), w.scale, causal)
@@ -55,7 +56,7 @@ def test_splitkv_on_underfilled_grid(fa, oracle_lib, nsplit):
     w = ai.WORKLOADS["c2"]
     inp = ai.make_inputs(w, with_do=False)
     dev = {k: v.cuda() for k, v in inp.items()}
-    parts = fa.fwd_splitkv_parts(w.B, w.H, w.N, nsplit)
+    parts = fa.fwd_splitkv_parts(w.B, w.H, w.N, nsplit, w.causal)
     assert parts == (1 if nsplit == 0 else nsplit), parts
     o, lse = fa.fwd_splitkv(dev["q"], dev["k"], dev["v"], w.scale, w.causal, nsplit)
     o1, lse1 = fa.fwd(dev["q"], dev["k"], dev["v"], w.scale, w.causal)
@@ -112,13 +113,13 @@ def test_lse_merge_matches_oracle(fa, oracle_lib, P, d, out):
 
 
 def test_splitkv_long_rows_small_grid(fa, oracle_lib):
-    """B1 H4 N8192 causal (256 query blocks, fewer than the chip's workgroup
-    slots): the library splits the keys; sampled rows of every head against
-    the row-wise oracle, including the first and last rows."""
+    """B1 H4 N8192 causal (128 paired query-block units, fewer than the
+    chip's compute units): the library splits the keys; sampled rows of every
+    head against the row-wise oracle, including the first and last rows."""
     w = ai.custom("split-long", 1, 4, 8192, 128, "bf16", True, seed=42)
     inp = ai.make_inputs(w, with_do=False)
     dev = {k: v.cuda() for k, v in inp.items()}
-    assert fa.fwd_splitkv_parts(w.B, w.H, w.N, 0) > 1
+    assert fa.fwd_splitkv_parts(w.B, w.H, w.N, 0, True) > 1
     o, lse = fa.fwd_splitkv(dev["q"], dev["k"], dev["v"], w.scale, True, 0)
     torch.cuda.synchronize()
     rng = np.random.default_rng(8)
