@@ -216,8 +216,19 @@ class ClockSampler:
                 "mfma_bf16_tflops_at_clock": round(256 * 4 * 1024 * med * 1e6 / 1e12, 1)}
 
 
-def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0, sampler=None):
-    """Returns (ms_per_step, ms_fwd_only, per-kernel ms dict, outputs, host inputs).
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0, sampler=None,
+                  fwd_runs=50):
+    """Times one workload. Returns a dict: ms_step (mean over the `steps` timed
+    steps, one event pair around all of them), ms_step_median (median of the
+    per-step times), ms_fwd and ms_fwd_median (forward alone, `fwd_runs`
+    launches), kern (mean per-kernel times of the steps, or None), outs (the
+    outputs of a last clean step) and host (the host inputs).
 
     After the `warmup` steps, further untimed steps run until `settle_s`
     seconds have passed since the first one: the GPU clock climbs from its
@@ -237,6 +248,8 @@ def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0, sa
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     names = ("fwd", "bwd_dq", "bwd_dkdv")
+    # Events between the launches of every step (they sit on the same stream
+    # and add no work); the step time is first event to last.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
           for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
@@ -245,27 +258,26 @@ def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0, sa
     t0.record()
     for s in range(steps):
         for i, f in enumerate(fns):
-            if per_kernel:
-                ev[s][i].record()
+            ev[s][i].record()
             f()
-        if per_kernel:
-            ev[s][-1].record()
+        ev[s][-1].record()
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
+    ms_step_median = _median([ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)])
     kern = None
     if per_kernel:
         kern = {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
                 for i, n in enumerate(names)}
     # forward alone
-    f0 = torch.cuda.Event(enable_timing=True)
-    f1 = torch.cuda.Event(enable_timing=True)
-    f0.record()
-    for _ in range(steps):
+    fe = [torch.cuda.Event(enable_timing=True) for _ in range(fwd_runs + 1)]
+    for r in range(fwd_runs):
+        fe[r].record()
         fns[0]()
-    f1.record()
+    fe[-1].record()
     torch.cuda.synchronize()
-    ms_fwd = f0.elapsed_time(f1) / steps
+    ms_fwd = fe[0].elapsed_time(fe[-1]) / fwd_runs
+    ms_fwd_median = _median([fe[r].elapsed_time(fe[r + 1]) for r in range(fwd_runs)])
     # one clean step so the outputs correspond to the inputs
     for f in fns:
         f()
@@ -274,7 +286,8 @@ def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0, sa
     # idle GPU lowers its clock before the forward-only launches above.
     if sampler is not None:
         sampler.clock = sampler.stop()
-    return ms_step, ms_fwd, kern, outs, host
+    return {"ms_step": ms_step, "ms_step_median": ms_step_median, "ms_fwd": ms_fwd,
+            "ms_fwd_median": ms_fwd_median, "kern": kern, "outs": outs, "host": host}
 
 
 def slice_errors(outs, b, h, o_ref, lse_ref, g):
@@ -318,6 +331,68 @@ def cpu_baseline(w, host, outs, min_seconds=10.0, max_slices=256):
             "kind": "oracle",
             "sample": "%d of %d (batch, head) slices of the workload, fwd+bwd in fp64 "
                       "(%.1f s)" % (n, w.B * w.H, t_total)}, worst
+
+
+# Whole (batch, head) slices of each workload the oracle is timed on: every
+# slice of the small ones, a sample of the large ones (about 1-3 s each).
+ORACLE_SLICES = {"c1": 1, "c2": 16, "c3": 4, "c4": 1, "c5": 8}
+
+
+def oracle_by_config(have=None):
+    """The fp64 oracle timed per workload on the host's cores (as many OpenMP
+    threads as it runs with), forward and, where the workload has one,
+    backward, on ORACLE_SLICES[name] whole slices; the whole workload's time
+    is that mean per slice times B*H (every slice has the same shape and
+    work). GFLOP/s use the pages' count (4 N^2 d forward, 10 N^2 d backward,
+    halved under the mask). Then c1 and c2 once more on one thread: the
+    per-core figure. `have`: host inputs already drawn, by workload name."""
+    import attn_inputs as ai
+    import oracle
+    have = have or {}
+    threads = oracle.num_threads()
+
+    def run(w, host, n):
+        t = 0.0
+        for i in range(n):
+            b, h = divmod(i * max(1, (w.B * w.H) // n), w.H)
+            q, k, v = (host[x][b, h].double().numpy() for x in ("q", "k", "v"))
+            t0 = time.perf_counter()
+            oracle.attention_fwd(q, k, v, w.scale, w.causal)
+            if w.backward:
+                oracle.attention_bwd(q, k, v, host["do"][b, h].double().numpy(), w.scale,
+                                     w.causal)
+            t += time.perf_counter() - t0
+        return t
+
+    out = []
+    for name, n in ORACLE_SLICES.items():
+        w = ai.WORKLOADS[name]
+        host = have.get(name) or ai.make_inputs(w, with_do=w.backward)
+        per_slice = w.fwd_flops() / (w.B * w.H)
+        if w.backward:
+            per_slice += w.bwd_flops() / (w.B * w.H)
+        t = run(w, host, n)
+        rec = {"workload": name, "pass": "fwd+bwd" if w.backward else "fwd",
+               "threads": threads, "slices_timed": n, "slices": w.B * w.H,
+               "seconds_timed": round(t, 3),
+               "seconds_whole_workload": round(t / n * w.B * w.H, 2),
+               "gflops": round(per_slice * n / t / 1e9, 2)}
+        if name in ("c1", "c2"):
+            oracle.set_num_threads(1)
+            try:
+                n1 = 1 if name == "c1" else 2
+                t1 = run(w, host, n1)
+            finally:
+                oracle.set_num_threads(threads)
+            rec["one_thread"] = {"slices_timed": n1, "seconds_timed": round(t1, 3),
+                                 "gflops": round(per_slice * n1 / t1 / 1e9, 3)}
+        out.append(rec)
+        print("# oracle %s: %d of %d slices in %.2f s on %d threads (%.2f GFLOP/s)%s" %
+              (name, n, w.B * w.H, t, threads, rec["gflops"],
+               "; one thread %.3f GFLOP/s" % rec["one_thread"]["gflops"]
+               if "one_thread" in rec else ""), file=sys.stderr, flush=True)
+        del host
+    return out
 
 
 def _time_ms(torch, fn, iters, settle_s):
@@ -535,8 +610,10 @@ def main():
 
     w = ai.WORKLOADS[args.workload]
     sampler = None if args.no_clock else ClockSampler()
-    ms_step, ms_fwd, kern, outs, host = time_workload(fa, torch, w, args.steps, args.warmup,
-                                                       settle_s=args.settle, sampler=sampler)
+    tw = time_workload(fa, torch, w, args.steps, args.warmup, settle_s=args.settle,
+                       sampler=sampler)
+    ms_step, ms_fwd, kern, outs, host = (tw["ms_step"], tw["ms_fwd"], tw["kern"], tw["outs"],
+                                         tw["host"])
     clock = sampler.clock if sampler is not None else {"samples": 0, "error": "--no-clock"}
     flops_step = w.fwd_flops() + w.bwd_flops()
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -580,6 +657,11 @@ def main():
                       "parallelism": "none (1 GPU)"},
            "fwd_tflops": round(fwd_tflops, 2),
            "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 2),
+           "median": {"fwd_tflops": round(w.fwd_flops() / tw["ms_fwd_median"] / 1e9, 2),
+                      "fwdbwd_tflops": round(flops_step / tw["ms_step_median"] / 1e9, 2),
+                      "fwd_runs": 50, "fwdbwd_runs": args.steps,
+                      "ms_fwd": round(tw["ms_fwd_median"], 4),
+                      "ms_fwdbwd": round(tw["ms_step_median"], 4)},
            "fwd_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
            "fwdbwd_frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
            "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
@@ -595,8 +677,11 @@ def main():
         for name in ("perf-2k", "perf-4k", "perf-8k", "perf-2k-causal", "perf-4k-causal",
                      "perf-8k-causal", "c3", "c4"):
             ws = ai.WORKLOADS[name]
-            s_ms, f_ms, _, _, _ = time_workload(fa, torch, ws, 10, 3, per_kernel=False,
-                                                  settle_s=min(args.settle, 1.0))
+            r = time_workload(fa, torch, ws, 20, 3, per_kernel=False,
+                              settle_s=min(args.settle, 1.0))
+            # Median of 20 fwd+bwd steps and of 50 forward launches.
+            s_ms, f_ms = r["ms_step_median"], r["ms_fwd_median"]
+            del r
             tf = (ws.fwd_flops() + ws.bwd_flops()) / (s_ms * 1e-3) / 1e12
             ff = ws.fwd_flops() / (f_ms * 1e-3) / 1e12
             sweep.append({"workload": name, "B": ws.B, "H": ws.H, "N": ws.N, "d": ws.d,
@@ -619,6 +704,7 @@ def main():
         cb, worst = cpu_baseline(w, host, outs)
         out["cpu_baseline"] = cb
         out["parity_spot_check"] = worst
+        out["oracle_by_config"] = oracle_by_config({w.name: host})
     print(json.dumps(out), flush=True)
 
 

@@ -106,12 +106,21 @@ def test_many_tiles_ragged(fa, oracle_lib, causal):
 # The five workloads at full size; sampled slices checked by the oracle
 # ---------------------------------------------------------------------------
 
+def _corners_and_random(B, H, extra, seed):
+    """The four corner (batch, head) slices and `extra` others drawn at random."""
+    corners = sorted({(0, 0), (0, H - 1), (B - 1, 0), (B - 1, H - 1)})
+    rest = [(b, h) for b in range(B) for h in range(H) if (b, h) not in corners]
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(len(rest), min(extra, len(rest)), replace=False)
+    return corners + sorted(rest[i] for i in pick)
+
+
 SAMPLES = {
     "c1": [(0, 0)],
     "c2": [(0, 0), (0, 5), (1, 2), (1, 7)],
-    "c3": [(0, 0), (2, 17), (3, 31)],
-    "c4": [(0, 0)],
-    "c5": [(0, 0), (15, 31)],
+    "c3": _corners_and_random(4, 32, 6, seed=3),
+    "c4": [(0, 0), (0, 7), (0, 15)],
+    "c5": _corners_and_random(16, 32, 8, seed=5),
 }
 
 
@@ -283,6 +292,56 @@ def test_gradient_sums_and_determinism(fa, name):
     assert float(sk.max()) <= 2e-2, float(sk.max())
     sv = (dv.sum(2) - do.sum(2)).norm(dim=-1) / do.sum(2).norm(dim=-1)
     assert float(sv.max()) <= 2e-2, float(sv.max())
+
+
+def _coarse(t):
+    """Values on the grid of multiples of 1/16 inside (-4, 4): sums of two such
+    values stay below 8 in magnitude and are exact in bf16 and fp16."""
+    return (torch.round(t.double() * 16).clamp(-63, 63) / 16).to(t.dtype).contiguous()
+
+
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_key_shift_invariance(fa, name):
+    """K_j -> K_j + c for every key j adds scale q_i . c to every score of
+    row i: P, and so O, dV and dK, are unchanged; LSE_i moves by scale q_i . c;
+    dQ moves by scale (sum_j dS_ij) c = 0 because the rows of dS sum to zero.
+    K and c are taken on a coarse grid so that K + c is exact in the dtype,
+    and the two runs differ only in the kernels' rounding."""
+    w = ai.WORKLOADS[name]
+    inp = ai.make_inputs(w)
+    inp["k"] = _coarse(inp["k"])
+    g = torch.Generator().manual_seed(17)
+    c = _coarse(torch.randn(w.B, w.H, 1, w.d, generator=g)).to(inp["k"].dtype)
+    shifted = dict(inp, k=(inp["k"].double() + c.double()).to(inp["k"].dtype).contiguous())
+    assert torch.equal(shifted["k"].double() - inp["k"].double(), c.double().expand_as(inp["k"]))
+    a = _run(fa, w, inp)
+    b = _run(fa, w, shifted)
+    assert max_abs(b["o"], a["o"]) <= 2e-2
+    assert rel_l2(b["o"], a["o"]) <= 4e-3
+    qc = w.scale * (inp["q"].double() * c.double()).sum(-1)    # scale q_i . c
+    assert max_abs(b["lse"].double() - a["lse"].double(), qc) <= 2e-3
+    for key in ("dq", "dk", "dv"):
+        r = rel_l2(b[key], a[key])
+        assert r <= 1e-2, (key, r)
+
+
+def test_joint_key_value_permutation(fa):
+    """Without the mask, permuting the rows of K and V together permutes the
+    terms of every row's sums only: O, LSE and dQ are unchanged, and dK, dV
+    come out permuted the same way (c3 at full size)."""
+    w = ai.WORKLOADS["c3"]
+    inp = ai.make_inputs(w)
+    perm = torch.randperm(w.N, generator=torch.Generator().manual_seed(23))
+    moved = dict(inp, k=inp["k"][:, :, perm].contiguous(), v=inp["v"][:, :, perm].contiguous())
+    a = _run(fa, w, inp)
+    b = _run(fa, w, moved)
+    assert max_abs(b["o"], a["o"]) <= 2e-2
+    assert rel_l2(b["o"], a["o"]) <= 4e-3
+    assert max_abs(b["lse"], a["lse"]) <= 1e-4
+    assert rel_l2(b["dq"], a["dq"]) <= 1e-2
+    for key in ("dk", "dv"):
+        r = rel_l2(b[key], a[key][:, :, perm])
+        assert r <= 1e-2, (key, r)
 
 
 def test_stages_match_fused_call(fa):
