@@ -14,7 +14,7 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_splitkv", "fwd_splitkv_parts", "fwd_splitkv_workspace_bytes",
-           "fwd_kvcache", "fwd_kvcache_parts", "fwd_kvcache_workspace_bytes", "lse_merge", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq",
+           "fwd_kvcache", "fwd_kvcache_parts", "fwd_kvcache_workspace_bytes", "lse_merge", "bwd", "bwd_noalloc", "bwd_preprocess", "bwd_dkdv", "bwd_dq",
            "bwd_workspace_bytes", "FAError", "library_path", "lib",
            "F32", "F16", "BF16"]
 
@@ -70,6 +70,8 @@ def lib():
     L.fa_bwd_workspace_bytes.restype = z
     L.fa_bwd.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, p, p, z, p]
     L.fa_bwd.restype = i
+    L.fa_bwd_noalloc.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, p, p]
+    L.fa_bwd_noalloc.restype = i
     L.fa_bwd_preprocess.argtypes = [i, i, i, i, i, p, p, p, p]
     L.fa_bwd_preprocess.restype = i
     L.fa_bwd_dkdv.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, p]
@@ -249,6 +251,23 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None):
     _call("fa_bwd", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
           _ptr(lse), _scale(scale, d), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, do, lse, scale=None, causal=False, out=None):
+    """bwd() through fa_bwd_noalloc: D lives in the library's static scratch
+    instead of a workspace. out: optional (dq, dk, dv) tensors to write into
+    (shaped like q, contiguous, on q's device); else they are allocated here."""
+    dt, B, H, N, d = _check_qkv(q, k, v, o, do)
+    _check_rows(lse, "lse", q)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    else:
+        _check_qkv(q, *out)
+    dq, dk, dv = out
+    _call("fa_bwd_noalloc", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+          _ptr(lse), _scale(scale, d), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
+          _stream(q))
     return dq, dk, dv
 
 

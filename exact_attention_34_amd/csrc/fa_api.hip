@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fa.h"
 #include "fa_launch.h"
 #include "fa_std_launch.h"
@@ -153,6 +155,60 @@ int check_std(int dtype, int B, int H, int N, int d) {
 }
 size_t std_ds_bytes(int B, int H, int N) { return round_up(std_elems(B, H, N) * 2, kWsAlign); }
 
+// Static scratch of fa_bwd_noalloc: D = rowsum(dO o O) for up to
+// FA_BWD_NOALLOC_MAX_ROWS rows (16 MiB), one copy per device, allocated when
+// the library's code object loads on that device and held until the process
+// ends. Host code never uses this name as an address: the device address of
+// each device's copy comes from hipGetSymbolAddress (scratch_on).
+__device__ __attribute__((aligned(256))) float scratch[FA_BWD_NOALLOC_MAX_ROWS];
+
+constexpr int kMaxDevices = 256;
+std::atomic<float *> g_scratch[kMaxDevices];
+
+// The device address of `scratch` on device dev, looked up once per device
+// with that device current (the lookup is the same on every call, so two
+// threads racing on the first call store the same value).
+int scratch_on(int dev, float **out) {
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  float *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_LAUNCH;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return FA_ERR_LAUNCH;
+    void *addr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return FA_ERR_LAUNCH;
+    if (e != hipSuccess || addr == nullptr) return FA_ERR_LAUNCH;
+    p = (float *)addr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return FA_OK;
+}
+
+// The device whose queue `stream` feeds (the current device for the null
+// stream): kernels run there, so the scratch must be that device's copy.
+int stream_device(hipStream_t st, int *dev) {
+  if (st == nullptr) return hipGetDevice(dev) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  hipDevice_t d = -1;
+  if (hipStreamGetDevice(st, &d) != hipSuccess) return FA_ERR_LAUNCH;
+  *dev = (int)d;
+  return FA_OK;
+}
+
+// fa_bwd's two sweeps with D at Dvec (already checked arguments).
+int run_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
+            const void *O, const void *dO, const float *LSE, float scale, int causal, void *dQ,
+            void *dK, void *dV, float *Dvec, hipStream_t st) {
+  // The dQ sweep forms D itself (as fa_bwd_preprocess would) and stores it
+  // for the dK/dV sweep that follows on the stream.
+  int rc = status(fa::launch_bwd_dq_fused(dtype, B, H, N, d, Q, K, V, O, dO, LSE, Dvec, scale,
+                                          causal, dQ, st));
+  if (rc != FA_OK) return rc;
+  return status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
+                                    dK, dV, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -166,6 +222,7 @@ const char *fa_status_str(int s) {
     case FA_ERR_UNSUPPORTED: return "unsupported head size or dtype";
     case FA_ERR_WORKSPACE: return "workspace too small";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_SCRATCH: return "problem larger than the static scratch (B*H*N rows)";
     default: return "unknown status";
   }
 }
@@ -323,15 +380,28 @@ int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, 
       !tensor_ok(workspace))
     return FA_ERR_INVALID_ARG;
   if (workspace_bytes < fa_bwd_workspace_bytes(dtype, B, H, N, d)) return FA_ERR_WORKSPACE;
-  float *Dvec = (float *)workspace;
+  return run_bwd(dtype, B, H, N, d, Q, K, V, O, dO, LSE, scale, causal, dQ, dK, dV,
+                 (float *)workspace, (hipStream_t)stream);
+}
+
+int fa_bwd_noalloc(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                   const void *V, const void *O, const void *dO, const float *LSE, float scale,
+                   int causal, void *dQ, void *dK, void *dV, void *stream) {
+  int rc = check_shape(dtype, B, H, N, d, true);
+  if (rc != FA_OK) return rc;
+  if ((rc = check_scale_causal(scale, causal)) != FA_OK) return rc;
+  if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O) || !tensor_ok(dO) ||
+      !vec_ok(LSE) || !tensor_ok(dQ) || !tensor_ok(dK) || !tensor_ok(dV))
+    return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * N > FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH;
   hipStream_t st = (hipStream_t)stream;
-  // The dQ sweep forms D itself (as fa_bwd_preprocess would) and stores it
-  // for the dK/dV sweep that follows on the stream.
-  if ((rc = status(fa::launch_bwd_dq_fused(dtype, B, H, N, d, Q, K, V, O, dO, LSE, Dvec, scale,
-                                           causal, dQ, st))) != FA_OK)
-    return rc;
-  return status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
-                                    dK, dV, st));
+  int dev = -1;
+  float *Dvec = nullptr;
+  if ((rc = stream_device(st, &dev)) != FA_OK) return rc;
+  if ((rc = scratch_on(dev, &Dvec)) != FA_OK) return rc;
+  // Every row of D is written by the dQ sweep before the dK/dV sweep reads
+  // it, so the scratch needs no clearing.
+  return run_bwd(dtype, B, H, N, d, Q, K, V, O, dO, LSE, scale, causal, dQ, dK, dV, Dvec, st);
 }
 
 int fa_std_row_stride(int N) { return N > 0 ? fa::std_row_stride(N) : 0; }

@@ -69,6 +69,11 @@ extern "C" {
 #define FA_ERR_UNSUPPORTED (-2) /* head size d or dtype not built */
 #define FA_ERR_WORKSPACE (-3)   /* workspace smaller than required */
 #define FA_ERR_LAUNCH (-4)      /* kernel launch failed */
+#define FA_ERR_SCRATCH (-5)     /* fa_bwd_noalloc: B*H*N above
+                                   FA_BWD_NOALLOC_MAX_ROWS */
+
+/* Rows (B*H*N) of the static scratch behind fa_bwd_noalloc. */
+#define FA_BWD_NOALLOC_MAX_ROWS (1 << 22)
 
 /* Version of this interface (FA_ABI_VERSION). */
 int fa_abi_version(void);
@@ -210,6 +215,30 @@ int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
            const void *V, const void *O, const void *dO, const float *LSE,
            float scale, int causal, void *dQ, void *dK, void *dV,
            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same inputs, outputs, kernels and
+ * results as fa_bwd (bit for bit). The fp32 D = rowsum(dO o O) that fa_bwd
+ * keeps in the caller's workspace lives instead in a static device array of
+ * the library, FA_BWD_NOALLOC_MAX_ROWS floats (16 MiB), one copy per device,
+ * allocated when the library's code loads on that device and held until the
+ * process ends; its address is looked up on the first call on each device
+ * (the device of `stream`; the current device for the null stream).
+ * Nothing is allocated or freed, by this call or by the library.
+ * Errors: as fa_bwd, plus FA_ERR_SCRATCH when B*H*N exceeds
+ *   FA_BWD_NOALLOC_MAX_ROWS (checked before anything is enqueued).
+ * Every call on one device shares that device's scratch: calls whose work
+ * overlaps on one device (several streams, or threads on one device) race
+ * on it and must be serialised by the caller. Nothing in the scratch needs
+ * clearing between calls: every row a call reads was written earlier in
+ * the same call.
+ */
+int fa_bwd_noalloc(int dtype, int B, int H, int N, int d, const void *Q,
+                   const void *K, const void *V, const void *O, const void *dO,
+                   const float *LSE, float scale, int causal, void *dQ,
+                   void *dK, void *dV, void *stream);
 
 /*
  * The three stages of fa_bwd, for callers that schedule them separately.

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert L.fa_abi_version() == _status("FA_ABI_VERSION")
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         s = L.fa_status_str(code).decode()
         assert s and s != "unknown status"
     assert L.fa_status_str(7).decode() == "unknown status"
@@ -102,6 +102,24 @@ def test_bwd_rejects(L):
     assert _bwd(L, lse=NUL) == INVALID
     need = L.fa_bwd_workspace_bytes(2, 1, 1, 16, 64)
     assert _bwd(L, ws_bytes=need - 1) == WS
+
+
+SCRATCH = _status("FA_ERR_SCRATCH")
+MAX_ROWS = 1 << 22   # FA_BWD_NOALLOC_MAX_ROWS
+
+
+def test_noalloc_rejects(L):
+    """fa_bwd_noalloc checks its arguments as fa_bwd does and refuses problems
+    with more rows than its static scratch holds, before any HIP call."""
+    nb = lambda dtype=2, B=1, H=1, N=16, d=64, scale=0.125, causal=0, dq=A2, lse=A2: \
+        L.fa_bwd_noalloc(dtype, B, H, N, d, A, A, A, A, A, lse, scale, causal, dq, A2, A2, None)
+    assert "(1 << 22)" in open(HEADER).read()
+    assert nb(dtype=0) == UNSUP and nb(d=32) == UNSUP
+    assert nb(N=0) == INVALID and nb(scale=-1.0) == INVALID and nb(causal=2) == INVALID
+    assert nb(dq=MIS) == INVALID and nb(lse=NUL) == INVALID
+    assert nb(B=1, H=1, N=MAX_ROWS + 1) == SCRATCH
+    assert nb(B=2, H=32, N=MAX_ROWS // 64 + 1) == SCRATCH
+    assert nb(B=64, H=64, N=1025, d=128) == SCRATCH
 
 
 def test_stage_entry_points_reject(L):
