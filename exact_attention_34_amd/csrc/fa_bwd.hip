@@ -160,67 +160,121 @@ struct DkdvCfg {
 // tiles (Q, dO, LSE, D) are triple-buffered (the tile being read, the
 // previous one for role 1's dK, and the next one being loaded).
 //
-// One key block (block kb of slice bh). Query-tile buffers: buffer b holds Q
-// at qo + 2*b*QTILE, dO right after it, and LSE, D rows at lv + 2*b*BR; px
-// is the P hand-over area, PX floats per key slice.
+// The stream of one workgroup. The kernel is persistent: workgroup w takes
+// the work units w, w + G, w + 2G, ... (G workgroups, one per compute unit
+// at most), each mapped XCD-aware as in the other sweeps. A unit is one key
+// block, or under the causal mask the pair of blocks p and nkb - 1 - p,
+// whose sweeps add up to the same length for every p. The workgroup walks
+// all (block, query tile) steps of its units as one stream, so the loads of
+// a block's first tiles and of its K and V rows are issued during the last
+// steps of the block before, and the dK and dV of a finished block are
+// stored while the next block computes. Position in the stream (wave-
+// uniform): virtual workgroup id v (the stream ends at v >= total), slice
+// bh, unit u, which block of the unit (half), key block kb, query tile it.
+struct DkdvPos {
+  int v, bh, u, half, kb, it;
+};
+
+// Steps of the workgroup's stream. Query-tile buffers rotate over the steps:
+// buffer b (step % 3) holds Q at qo + 2*b*QTILE, dO right after it, and LSE,
+// D rows at lv + 2*b*BR; px is the P hand-over area, PX floats per key slice.
+//
+// The direct loads of a step's tile are issued during the step before, by
+// role 0 normally, but by role 1 for the first two steps after a block ends;
+// each wave waits only for loads it issued itself (then the barrier). At the
+// end of a block role 0 stores dV and role 1 stores dK one step later, and
+// neither waits for those stores before its next wait on loads of its own:
+// a wave never issues tile loads in the two steps after it stored, so its
+// waits never include store latency. (Vector-memory loads and stores of a
+// wave share one counter and may complete out of order with each other, so
+// a wait for loads alone is only possible when no store is outstanding.)
 template <typename T, int D, bool CAUSAL>
-__device__ __forceinline__ void dkdv_block(
+__global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dK,
-    uint16_t *__restrict__ dV, int N, int bh, int kb, float c2, float scale, uint16_t *qo,
-    float *lv, float *px) {
+    uint16_t *__restrict__ dV, int N, int nkb, int nunits, int total, float c2, float scale) {
   using C = DkdvCfg<D>;
   constexpr int NT = C::NT;
+  __shared__ __attribute__((aligned(1024))) uint16_t qo[2 * C::NBUF * C::QTILE];
+  __shared__ __attribute__((aligned(256))) float lv[2 * C::NBUF * C::BR];
+  __shared__ __attribute__((aligned(1024))) float px[4 * C::PX];
+  // Output staging: 32 keys x 64 columns (16-bit) per key slice, used by the
+  // slice's two waves at different times (separated by barriers).
+  __shared__ __attribute__((aligned(1024))) uint16_t stage[4 * 32 * 64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int l32 = lane & 31, g = lane >> 5;
-  const int ks = w & 3;     // key slice: keys 32 ks .. +31 of the block
+  const int ks = w & 3;     // key slice: keys 32 ks .. +31 of a block
   const int role = w >> 2;  // 0: S, P, dV; 1: dP, dS, dK
-  const int k0 = kb * C::KB;
-  const int wk0 = k0 + 32 * ks;  // first key of this wave
-  const int mykey = wk0 + l32;   // key of this lane's S/P column
-  const size_t base = (size_t)bh * N * D;
-  const uint16_t *Qh = Q + base, *dOh = dO + base;
+  const int nq = (N + C::BR - 1) / C::BR;
+  const int G = gridDim.x;
 
-  // This slice's K (role 0) or V (role 1) rows as the B operand: lane l holds
-  // key mykey, 8 consecutive columns 16c + 8g .. per chunk c. Keys past N
-  // read row N - 1 (masked).
+  auto block_start = [&](int kb) { return CAUSAL ? kb * C::KB / C::BR : 0; };
+  auto unit_pos = [&](int v) {
+    DkdvPos p;
+    p.v = v;
+    const int t = v < total ? xcd_tile(v, total) : 0;
+    p.bh = t / nunits;
+    p.u = t - p.bh * nunits;
+    p.half = 0;
+    p.kb = p.u;
+    p.it = block_start(p.u);
+    return p;
+  };
+  auto advance = [&](DkdvPos p) {
+    if (p.it + 1 < nq) {
+      ++p.it;
+      return p;
+    }
+    if (CAUSAL && p.half == 0 && p.u != nkb - 1 - p.u) {
+      p.half = 1;
+      p.kb = nkb - 1 - p.u;
+      p.it = block_start(p.kb);
+      return p;
+    }
+    return unit_pos(p.v + G);
+  };
+  auto last_of_block = [&](const DkdvPos &p) { return p.it == nq - 1; };
+
+  // This slice's K (role 0) or V (role 1) rows as the B operand: lane l
+  // holds key kb*KB + 32 ks + l%32, 8 consecutive columns 16c + 8g .. per
+  // chunk c. Keys past N read row N - 1 (masked).
   u32x4 kv[C::NCH];
-  {
-    const uint16_t *src = (role == 0 ? K : V) + base + (size_t)min(mykey, N - 1) * D;
+  auto load_rows = [&](const DkdvPos &p) __attribute__((always_inline)) {
+    const int key = min(p.kb * C::KB + 32 * ks + l32, N - 1);
+    const uint16_t *src = (role == 0 ? K : V) + (size_t)p.bh * N * D + (size_t)key * D;
 #pragma unroll
     for (int c = 0; c < C::NCH; ++c) kv[c] = ld128(src + 16 * c + 8 * g);
-  }
+  };
 
-  const int nq = (N + C::BR - 1) / C::BR;
-  const int it0 = CAUSAL ? k0 / C::BR : 0;  // earlier queries see none of these keys
-
-  // Direct buffer -> LDS loads of a query tile, issued by the role-0 waves
-  // (which have slack while their partners finish dK and dP): instruction i
-  // of wave w fills LDS chunks (w*LPW + i)*64 + lane with the global chunk
-  // the swizzle puts there. Waves 0 .. 2*BR/64-1 also load 64 LSE or D
-  // values each. The buffer resources cover the rows that exist; rows past
-  // N read as zero (and are masked).
+  // Direct buffer -> LDS loads of the query tile of step p into buffer b,
+  // by the four waves of one role (r = w & 3): instruction i of wave r fills
+  // LDS chunks (r*LPW + i)*64 + lane with the global chunk the swizzle puts
+  // there; waves r < 2*BR/64 also load 64 LSE or D values each. The buffer
+  // resources cover the rows that exist; rows past N read as zero (and are
+  // masked).
+  const int r4 = w & 3;
   int gq[C::LPW];
 #pragma unroll
-  for (int i = 0; i < C::LPW; ++i) gq[i] = src_of_chunk<D>((w * C::LPW + i) * 64 + lane);
+  for (int i = 0; i < C::LPW; ++i) gq[i] = src_of_chunk<D>((r4 * C::LPW + i) * 64 + lane);
   constexpr int kVecParts = C::BR / 64;
-  auto issue = [&](int b, int it) __attribute__((always_inline)) {
+  auto issue = [&](int b, const DkdvPos &p) __attribute__((always_inline)) {
     uint16_t *Qb = qo + 2 * b * C::QTILE, *Ob = Qb + C::QTILE;
-    const int q0 = it * C::BR;
+    const int q0 = p.it * C::BR;
     const int rows = min(N - q0, C::BR);
-    const i32x4 qrs = make_rsrc(Qh + (size_t)q0 * D, (uint32_t)rows * D * 2);
-    const i32x4 ors = make_rsrc(dOh + (size_t)q0 * D, (uint32_t)rows * D * 2);
+    const size_t base = (size_t)p.bh * N * D + (size_t)q0 * D;
+    const i32x4 qrs = make_rsrc(Q + base, (uint32_t)rows * D * 2);
+    const i32x4 ors = make_rsrc(dO + base, (uint32_t)rows * D * 2);
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
-      dma_lds16(qrs, gq[i], 0, Qb + (w * C::LPW + i) * 512);
-      dma_lds16(ors, gq[i], 0, Ob + (w * C::LPW + i) * 512);
+      dma_lds16(qrs, gq[i], 0, Qb + (r4 * C::LPW + i) * 512);
+      dma_lds16(ors, gq[i], 0, Ob + (r4 * C::LPW + i) * 512);
     }
-    if (w < 2 * kVecParts) {
-      const int vec = w / kVecParts, part = w % kVecParts;
+    if (r4 < 2 * kVecParts) {
+      const int vec = r4 / kVecParts, part = r4 % kVecParts;
       const i32x4 vrs =
-          make_rsrc((vec == 0 ? LSE : Dvec) + (size_t)bh * N + q0, (uint32_t)rows * 4);
+          make_rsrc((vec == 0 ? LSE : Dvec) + (size_t)p.bh * N + q0, (uint32_t)rows * 4);
       dma_lds4(vrs, 4 * (64 * part + lane), 0, lv + 2 * b * C::BR + vec * C::BR + 64 * part);
     }
   };
@@ -286,33 +340,77 @@ __device__ __forceinline__ void dkdv_block(
         for (int h = 0; h < 4; ++h)
           pb[t][cc][h] = pack2<T>(x[t][8 * cc + 2 * h], x[t][8 * cc + 2 * h + 1]);
   };
-
-  // Tile `it` (in buffer b = (it - it0) % 3): wait for this wave's loads,
-  // barrier (every wave's loads landed; every wave is done with tile it - 2
-  // and with the P of the previous tile). The next tile's loads go into the
-  // buffer of tile it - 2 (role 0, later in the step).
-  auto top = [&]() __attribute__((always_inline)) {
-    wait_vmem_all();
-    __syncthreads();
-  };
   // rows of subtile t, register r: 8(r/4) + 4g + r%4; LSE and D of rows
   // 8i + 4g + (0..3) are consecutive in LDS, read as one 16-byte word.
   auto vec4 = [&](const float *Lb, int off, int t, int i) __attribute__((always_inline)) {
     return *(const f32x4 *)(Lb + off + 32 * t + 8 * i + 4 * g);
   };
-
+  // dK = scale * dK (role 1) or dV (role 0) of block (bh, kb), in halves of
+  // 64 columns transposed through this slice's staging area, so that every
+  // store instruction writes whole 128-byte lines (8 lanes of 16 bytes per
+  // row; storing straight from the accumulator layout -- 8 bytes of each of
+  // 32 rows per instruction -- cost 8 partial-line writes per line). In the
+  // staging area row r (key) holds 8 chunks of 16 bytes, chunk c at
+  // position c ^ (r % 8), which spreads both access patterns over the banks.
   f32x16 acc[C::NDT];  // dV^T (role 0) or dK^T (role 1): column = key, rows = d
+  char *stg = (char *)(stage + ks * 32 * 64);
+  auto store_acc = [&](int bh, int kb) __attribute__((always_inline)) {
+    const float f = role == 0 ? 1.f : scale;
+    uint16_t *out = (role == 0 ? dV : dK) + (size_t)bh * N * D;
+    const int key0 = kb * C::KB + 32 * ks;
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h) {
+      // This lane's key (row l%32), columns 32 dtl + 8 i + 4 g .. +3 of the half.
+#pragma unroll
+      for (int dtl = 0; dtl < 2; ++dtl)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dt = 2 * h + dtl, c = 4 * dtl + i;
+          u32x2 a;
+          a[0] = pack2<T>(acc[dt][4 * i] * f, acc[dt][4 * i + 1] * f);
+          a[1] = pack2<T>(acc[dt][4 * i + 2] * f, acc[dt][4 * i + 3] * f);
+          *(u32x2 *)(stg + l32 * 128 + 16 * (c ^ (l32 & 7)) + 8 * g) = a;
+        }
+      // Rows 8k + lane/8, chunk lane % 8: 16 bytes per lane, 8 rows per
+      // instruction.
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + (lane >> 3), c = lane & 7;
+        const u32x4 v = *(const u32x4 *)(stg + r * 128 + 16 * (c ^ (r & 7)));
+        if (key0 + r < N) st128(out + (size_t)(key0 + r) * D + 64 * h + 8 * c, v);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) acc[dt] = kZero16;
+  };
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) acc[dt] = kZero16;
 
-  if (role == 0 && it0 < nq) issue(0, it0);
+  // Who loads the tile of step n: role 1 if the step before n or the one
+  // before that ended a block (lastA: step n-1, lastB: step n-2), else role 0.
+  auto loader = [](bool lastA, bool lastB) { return (lastA || lastB) ? 1 : 0; };
+
+  DkdvPos cur = unit_pos(blockIdx.x);
+  load_rows(cur);
+  if (role == 0) issue(0, cur);
+  bool mine = role == 0;     // this wave issued the loads of the current step
+  bool prev_last = false;    // the step before the current one ended a block
+  int b = 0;
+
   if (role == 0) {
-    for (int it = it0, b = 0; it < nq; ++it, b = (b == 2 ? 0 : b + 1)) {
-      top();
+    for (;;) {
+      if (mine) wait_vmem_all();
+      barrier_lds();  // every wave's loads landed; every wave is done with step - 2's buffer
       const uint16_t *Qs = qo + 2 * b * C::QTILE, *Os = Qs + C::QTILE;
       const float *Lb = lv + 2 * b * C::BR;
-      const int q0 = it * C::BR;
+      const int q0 = cur.it * C::BR;
+      const int wk0 = cur.kb * C::KB + 32 * ks;  // first key of this wave
+      const int mykey = wk0 + l32;               // key of this lane's S/P column
       const bool need_mask = (q0 + C::BR > N) || (wk0 + 32 > N) || (CAUSAL && wk0 + 31 > q0);
+      const bool last = last_of_block(cur);
+      const DkdvPos nxt = advance(cur);
+      const bool more = nxt.v < total;
+      const int bn = b == 2 ? 0 : b + 1;
       f32x4 lse[NT][4];
 #pragma unroll
       for (int t = 0; t < NT; ++t)
@@ -322,6 +420,8 @@ __device__ __forceinline__ void dkdv_block(
       f32x16 s[NT];
       rows_x_kv(s, Qs);  // S = Q K^T
       pipeline(KR{}, I1{}, I6{});
+      // The next block's K rows, into the registers the products above read.
+      if (last && more) load_rows(nxt);
       if (need_mask) {
         // Query q0 + 4g + off sees this lane's key iff lo <= off <= hi.
         const int hi = (mykey < N ? N - 1 : -1) - q0 - 4 * g;
@@ -351,25 +451,57 @@ __device__ __forceinline__ void dkdv_block(
           for (int j = 0; j < 4; ++j) s[t][4 * i + j] = p[j];
         }
       pack_b(s, pp);
-      if (it + 1 < nq) issue(b == 2 ? 0 : b + 1, it + 1);
+      const bool next_mine = more && loader(last, prev_last) == 0;
+      if (next_mine) issue(bn, nxt);
       barrier_lds();  // P visible to the partner
       tr_x_b(acc, Os, pp);  // dV^T += dO^T P
       pipeline(KT{}, I2{}, I4{});
+      if (last) {
+        // The K rows of the next block (loaded above) are waited for here,
+        // before the stores, so that no later wait includes the stores.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        store_acc(cur.bh, cur.kb);
+      }
+      if (!more) break;
+      mine = next_mine;
+      prev_last = last;
+      cur = nxt;
+      b = bn;
     }
+    barrier_lds();  // role 1 stages its last dK after this wave's last dV
   } else {
-    u32x4 pd[NT][2];  // dS of the previous tile, rounded to T
+    u32x4 pd[NT][2];  // dS of the previous step, rounded to T
     const uint16_t *Qprev = qo;
-    for (int it = it0, b = 0; it < nq; ++it, b = (b == 2 ? 0 : b + 1)) {
-      top();
+    int acc_bh = -1, acc_kb = -1;  // block whose dK the accumulator holds
+    int prev_bh = 0, prev_kb = 0;  // block of the previous step
+    bool have_prev = false;
+    for (;;) {
+      if (mine) wait_vmem_all();
+      barrier_lds();
       const uint16_t *Qs = qo + 2 * b * C::QTILE, *Os = Qs + C::QTILE;
       const float *Lb = lv + 2 * b * C::BR;
-      if (it > it0) {
-        tr_x_b(acc, Qprev, pd);  // dK^T += Q^T dS of the previous tile
+      const bool last = last_of_block(cur);
+      const DkdvPos nxt = advance(cur);
+      const bool more = nxt.v < total;
+      const int bn = b == 2 ? 0 : b + 1;
+      const bool next_mine = more && loader(last, prev_last) == 1;
+      // The buffer of step - 2 is free (every wave passed the barrier
+      // above after its last use): load the next step's tile into it.
+      if (next_mine) issue(bn, nxt);
+      if (have_prev) {
+        if (acc_bh != prev_bh || acc_kb != prev_kb) {
+          if (acc_bh >= 0) store_acc(acc_bh, acc_kb);
+          acc_bh = prev_bh;
+          acc_kb = prev_kb;
+        }
+        tr_x_b(acc, Qprev, pd);  // dK^T += Q^T dS of the previous step
         pipeline(KT{}, I2{}, I4{});
       }
       f32x16 dp[NT];
       rows_x_kv(dp, Os);  // dP = dO V^T
       pipeline(KR{}, I1{}, I6{});
+      // The next block's V rows, into the registers the products above read.
+      if (last && more) load_rows(nxt);
       barrier_lds();  // the partner's P is in LDS
       // dS = P o (dP - D), rounded to T.
 #pragma unroll
@@ -384,52 +516,22 @@ __device__ __forceinline__ void dkdv_block(
       pack_b(dp, pd);
       __builtin_amdgcn_sched_barrier(0);
       Qprev = Qs;
+      prev_bh = cur.bh;
+      prev_kb = cur.kb;
+      have_prev = true;
+      if (!more) break;
+      mine = next_mine;
+      prev_last = last;
+      cur = nxt;
+      b = bn;
     }
-    if (it0 < nq) {
-      tr_x_b(acc, Qprev, pd);  // dK^T += Q^T dS of the last tile
-      pipeline(KT{}, I2{}, I4{});
+    barrier_lds();  // the partner's last dV left the staging area
+    if (acc_bh != prev_bh || acc_kb != prev_kb) {
+      if (acc_bh >= 0) store_acc(acc_bh, acc_kb);
     }
-  }
-
-  // dK = scale * dK (role 1), dV (role 0); lane holds 4 consecutive columns
-  // per row.
-  if (mykey < N) {
-    uint16_t *row = (role == 0 ? dV : dK) + base + (size_t)mykey * D;
-    const float f = role == 0 ? 1.f : scale;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 a;
-        a[0] = pack2<T>(acc[dt][4 * i] * f, acc[dt][4 * i + 1] * f);
-        a[1] = pack2<T>(acc[dt][4 * i + 2] * f, acc[dt][4 * i + 3] * f);
-        *(u32x2 *)(row + 32 * dt + 8 * i + 4 * g) = a;
-      }
-  }
-}
-
-// Work units: without the causal mask, one key block. With it, key block kb
-// sweeps the query tiles from its own first row on, so blocks are paired as
-// (p, nkb - 1 - p), which gives every unit the same number of query tiles
-// (as in the forward).
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dK,
-    uint16_t *__restrict__ dV, int N, int nkb, int nunits, int total, float c2, float scale) {
-  using C = DkdvCfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint16_t qo[2 * C::NBUF * C::QTILE];
-  __shared__ __attribute__((aligned(256))) float lv[2 * C::NBUF * C::BR];
-  __shared__ __attribute__((aligned(1024))) float px[4 * C::PX];
-  const int tile = xcd_tile(blockIdx.x, total);
-  const int bh = tile / nunits;
-  const int u = tile - bh * nunits;
-  dkdv_block<T, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dK, dV, N, bh, u, c2, scale, qo, lv, px);
-  if (CAUSAL && u != nkb - 1 - u) {
-    __syncthreads();  // every wave is done with the LDS tiles
-    dkdv_block<T, D, CAUSAL>(Q, K, V, dO, LSE, Dvec, dK, dV, N, bh, nkb - 1 - u, c2, scale, qo,
-                             lv, px);
+    tr_x_b(acc, Qprev, pd);  // dK^T += Q^T dS of the last step
+    pipeline(KT{}, I2{}, I4{});
+    store_acc(prev_bh, prev_kb);
   }
 }
 
@@ -718,7 +820,15 @@ static hipError_t dkdv(const BwdArgs &a, void *dK, void *dV, hipStream_t st) {
   const int nkb = (a.N + C::KB - 1) / C::KB;
   const int nunits = CAUSAL ? (nkb + 1) / 2 : nkb;
   const int total = nunits * a.BH;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
+  // Persistent: one workgroup per compute unit (its LDS allows no second),
+  // or one per unit if there are fewer units.
+  int cus = 256, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  const int grid = min(total, cus);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(C::kThreads), 0, st,
                      a.Q, a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N, nkb,
                      nunits, total, a.c2, a.scale);
   return hipGetLastError();
