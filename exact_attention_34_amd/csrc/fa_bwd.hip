@@ -743,20 +743,12 @@ __device__ __forceinline__ void dq_block(
   if constexpr (CAUSAL)
     for (int kt = nmain; kt < ntiles; ++kt) sweep_tile(kt, std::true_type{});
 
-  // dQ = scale * dQ^T, transposed back: lane holds 4 consecutive columns of
-  // its row per register group.
-  if (qrow < N) {
-    uint16_t *dQrow = dQ + base + (size_t)qrow * D;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 v;
-        v[0] = pack2<T>(dq[dt][4 * i] * scale, dq[dt][4 * i + 1] * scale);
-        v[1] = pack2<T>(dq[dt][4 * i + 2] * scale, dq[dt][4 * i + 3] * scale);
-        *(u32x2 *)(dQrow + 32 * dt + 8 * i + 4 * g) = v;
-      }
-  }
+  // dQ = scale * dQ^T, transposed back and stored in whole rows through
+  // this wave's 32-row share of the K/V buffers (store_tile_rows), once no
+  // wave reads the tiles and no direct load still writes them.
+  wait_vmem_all();
+  __syncthreads();
+  store_tile_rows<T, D>(dq, scale, kv + w * 32 * D, dQ + base + (size_t)wq0 * D, N - wq0, lane);
 }
 
 // Work units as in the forward: one query block, or under the causal mask

@@ -245,6 +245,44 @@ __device__ __forceinline__ void barrier_lds() {
 // Wait until every vector-memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Stores a wave's 32 x D output tile, held in the layout of D/32 MFMA
+// results (lane l: row l % 32; acc[dt] register r: column
+// 32 dt + 8 (r / 4) + 4 (l / 32) + r % 4), times f and rounded to T, into
+// rows 0 .. nrows-1 of a dense row-major [*, D] array at out. It goes
+// through `lds`, a wave-private area of 32 * D 16-bit elements (16-byte
+// aligned): straight from the accumulator layout a store instruction would
+// write 8 bytes into each of 32 rows (a 128-byte line then takes 8 partial
+// writes); read back row-major, each instruction writes 64 / (D/8) whole rows,
+// 16 bytes per lane. In the LDS area row r holds its 16-byte chunks c at
+// position c ^ (r % CPR), which spreads both access patterns over the banks.
+// The caller makes sure no other wave uses the area meanwhile.
+template <typename T, int D>
+__device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[D / 32], float f,
+                                                uint16_t *lds, uint16_t *out, int nrows,
+                                                int lane) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  char *st = (char *)lds;
+  const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 4 * dt + i;  // chunk of columns 32 dt + 8 i .. +7
+      u32x2 a;
+      a[0] = pack2<T>(acc[dt][4 * i] * f, acc[dt][4 * i + 1] * f);
+      a[1] = pack2<T>(acc[dt][4 * i + 2] * f, acc[dt][4 * i + 3] * f);
+      *(u32x2 *)(st + l32 * 2 * D + 16 * (c ^ (l32 % CPR)) + 8 * g) = a;
+    }
+  // 64 lanes x 16 bytes = 64 / CPR rows per instruction.
+  constexpr int RPI = 64 / CPR;
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int r = RPI * k + lane / CPR, c = lane % CPR;
+    const u32x4 v = *(const u32x4 *)(st + r * 2 * D + 16 * (c ^ (r % CPR)));
+    if (r < nrows) *(u32x4 *)(out + (size_t)r * D + 8 * c) = v;
+  }
+}
+
 __device__ __forceinline__ u32x4 cat(const u32x2 &a, const u32x2 &b) {
   u32x4 r = {a[0], a[1], b[0], b[1]};
   return r;

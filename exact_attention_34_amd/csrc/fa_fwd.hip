@@ -429,19 +429,14 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
     }
     return;
   }
-  if (qrow < Nq) {
-    uint16_t *Orow = O + base + (size_t)qrow * D;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 v;
-        v[0] = pack2<T>(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv);
-        v[1] = pack2<T>(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
-        *(u32x2 *)(Orow + 32 * dt + 8 * i + 4 * g) = v;
-      }
-    if (g == 0) LSE[(size_t)bh * Nq + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
-  }
+  // O goes out through LDS in whole rows (store_tile_rows), each wave
+  // through its own 32-row half of a K or V tile buffer: wait until no wave
+  // reads the tiles and no direct load still writes them.
+  wait_vmem_all();
+  __syncthreads();
+  uint16_t *stg = (w >> 1 == 0 ? K0 : w >> 1 == 1 ? K1 : w >> 1 == 2 ? V0 : V1) + (w & 1) * 32 * D;
+  store_tile_rows<T, D>(o, inv, stg, O + base + (size_t)wq0 * D, Nq - wq0, lane);
+  if (qrow < Nq && g == 0) LSE[(size_t)bh * Nq + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
 // Work units: without the causal mask, one query block. With it, block qb
