@@ -305,16 +305,22 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
   using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
   using I6 = std::integral_constant<int, 6>;
+  // d = 64 (half the MFMAs per step, the same vector work): role 1 forms
+  // D - dP on the MFMAs, from negated V rows and D as the initial
+  // accumulator, which saves a subtraction per score after the hand-over
+  // (below).
+  constexpr bool kNegV = D == 64;
 
-  // One product with an operand read row-wise from a tile: acc[t] = Σ_c
-  // tile rows (32t + l%32, chunk c) x kv[c].
-  auto rows_x_kv = [&](f32x16 (&acc)[NT], const uint16_t *tile) __attribute__((always_inline)) {
+  // One product with an operand read row-wise from a tile: acc[t] = init[t]
+  // + Σ_c tile rows (32t + l%32, chunk c) x kv[c].
+  auto rows_x_kv = [&](f32x16 (&acc)[NT], const f32x16 (&init)[NT], const uint16_t *tile)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int c = 0; c < C::NCH; ++c)
         acc[t] = mfma32<T>(ld128(at(tile + 32 * D * t, rb ^ (32 * c))), kv[c],
-                           c == 0 ? kZero16 : acc[t]);
+                           c == 0 ? init[t] : acc[t]);
   };
   // acc^T += tile^T x B for B in the P / dS layout (pb[t][cc]).
   auto tr_x_b = [&](f32x16 (&acc)[C::NDT], const uint16_t *tile, const u32x4 (&pb)[NT][2])
@@ -355,7 +361,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
   f32x16 acc[C::NDT];  // dV^T (role 0) or dK^T (role 1): column = key, rows = d
   char *stg = (char *)(stage + ks * 32 * 64);
   auto store_acc = [&](int bh, int kb) __attribute__((always_inline)) {
-    const float f = role == 0 ? 1.f : scale;
+    // At d = 64 role 1 accumulates -dK (its dS carries the sign, below).
+    const float f = role == 0 ? 1.f : (kNegV ? -scale : scale);
     uint16_t *out = (role == 0 ? dV : dK) + (size_t)bh * N * D;
     const int key0 = kb * C::KB + 32 * ks;
 #pragma unroll
@@ -418,7 +425,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
         for (int i = 0; i < 4; ++i) lse[t][i] = vec4(Lb, 0, t, i);
       __builtin_amdgcn_sched_barrier(0);
       f32x16 s[NT];
-      rows_x_kv(s, Qs);  // S = Q K^T
+      const f32x16 zero[NT] = {};
+      rows_x_kv(s, zero, Qs);  // S = Q K^T
       pipeline(KR{}, I1{}, I6{});
       // The next block's K rows, into the registers the products above read.
       if (last && more) load_rows(nxt);
@@ -498,21 +506,58 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
         pipeline(KT{}, I2{}, I4{});
       }
       f32x16 dp[NT];
-      rows_x_kv(dp, Os);  // dP = dO V^T
+      if constexpr (kNegV) {
+        // This block's V rows, negated once (sign bits of both 16-bit
+        // halves) in the block's first step, where they are first read.
+        if (cur.it == block_start(cur.kb)) {
+#pragma unroll
+          for (int c = 0; c < C::NCH; ++c)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) kv[c][h] ^= 0x80008000u;
+        }
+        // E = D - dO V^T: the product accumulated onto D, D of row
+        // 32t + 8i + 4g + j in register 4i + j.
+        f32x16 dinit[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 dd = vec4(Lb, C::BR, t, i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dinit[t][4 * i + j] = dd[j];
+          }
+        rows_x_kv(dp, dinit, Os);
+      } else {
+        const f32x16 zero[NT] = {};
+        rows_x_kv(dp, zero, Os);  // dP = dO V^T
+      }
       pipeline(KR{}, I1{}, I6{});
       // The next block's V rows, into the registers the products above read.
       if (last && more) load_rows(nxt);
       barrier_lds();  // the partner's P is in LDS
-      // dS = P o (dP - D), rounded to T.
+      if constexpr (kNegV) {
+        // -dS = P o E = -(P o (dP - D)), rounded to T (rounding commutes
+        // with the sign, so the dK accumulated from it is exactly -dK).
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 p = *(const f32x4 *)(pxs + ((t * 4 + i) * 64 + lane) * 4);
-          const f32x4 dd = vec4(Lb, C::BR, t, i);
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 p = *(const f32x4 *)(pxs + ((t * 4 + i) * 64 + lane) * 4);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) dp[t][4 * i + j] = p[j] * (dp[t][4 * i + j] - dd[j]);
-        }
+            for (int j = 0; j < 4; ++j) dp[t][4 * i + j] = p[j] * dp[t][4 * i + j];
+          }
+      } else {
+        // dS = P o (dP - D), rounded to T.
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 p = *(const f32x4 *)(pxs + ((t * 4 + i) * 64 + lane) * 4);
+            const f32x4 dd = vec4(Lb, C::BR, t, i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dp[t][4 * i + j] = p[j] * (dp[t][4 * i + j] - dd[j]);
+          }
+      }
       pack_b(dp, pd);
       __builtin_amdgcn_sched_barrier(0);
       Qprev = Qs;
