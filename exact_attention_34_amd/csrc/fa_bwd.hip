@@ -693,18 +693,28 @@ __device__ __forceinline__ void dq_block(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[dt][r] = 0.f;
 
+  // d = 64 (half the MFMAs of d = 128 per score, the same vector work): dP^T
+  // starts from -D in every register, so that the MFMAs return dP - D and
+  // dS costs one multiply per score.
+  constexpr bool kDinit = D == 64;
+  f32x16 dneg;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dneg[r] = -dd;
+
   // One 32-key half t of a tile. need_mask: the half holds keys past N or
   // (causal) past this wave's first query row. The mask is a VALU-only
   // branch, so every MFMA accumulation runs on one code path.
   auto half = [&](const uint16_t *Ks, const uint16_t *Vs, int kb, int t, bool need_mask)
       __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    // S^T = K Q^T and dP^T = V dO^T; lane: query qrow, keys 8(r/4)+4g+r%4.
+    // S^T = K Q^T and dP^T = V dO^T (minus D when kDinit); lane: query
+    // qrow, keys 8(r/4)+4g+r%4.
     f32x16 s = kZero16, dp = kZero16;
 #pragma unroll
     for (int c = 0; c < C::NCH; ++c) {
       s = mfma32<T>(ld128(at(Ks + 32 * D * t, rb ^ (32 * c))), qreg[c], c == 0 ? kZero16 : s);
-      dp = mfma32<T>(ld128(at(Vs + 32 * D * t, rb ^ (32 * c))), oreg[c], c == 0 ? kZero16 : dp);
+      dp = mfma32<T>(ld128(at(Vs + 32 * D * t, rb ^ (32 * c))), oreg[c],
+                     c == 0 ? (kDinit ? dneg : kZero16) : dp);
     }
     // One operand read per MFMA, issued four MFMAs ahead.
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -733,7 +743,10 @@ __device__ __forceinline__ void dq_block(
         const int r = 8 * cc + 2 * h;
         const float p0 = fast_exp2(__builtin_fmaf(s[r], c2, -lse2));
         const float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c2, -lse2));
-        pk[cc][h] = pack2<T>(p0 * (dp[r] - dd), p1 * (dp[r + 1] - dd));
+        if constexpr (kDinit)
+          pk[cc][h] = pack2<T>(p0 * dp[r], p1 * dp[r + 1]);
+        else
+          pk[cc][h] = pack2<T>(p0 * (dp[r] - dd), p1 * (dp[r + 1] - dd));
       }
     // dQ^T += K^T dS^T
 #pragma unroll
