@@ -620,7 +620,8 @@ def main():
     fwd_tflops = w.fwd_flops() / (ms_fwd * 1e-3) / 1e12
 
     # Algorithmic flops per launch of each backward sweep (see the header).
-    sweeps = {"bwd_dkdv": ("bwd_dkdv_kernel", 0.8 * w.bwd_flops()),
+    sweeps = {"bwd_dkdv": ("bwd_dkdv64_kernel" if w.d == 64 else "bwd_dkdv_kernel",
+                           0.8 * w.bwd_flops()),
               "bwd_dq": ("bwd_dq_kernel", 0.2 * w.bwd_flops())}
     dom = max(sweeps, key=lambda k: kern[k])
     kname, kflops = sweeps[dom]

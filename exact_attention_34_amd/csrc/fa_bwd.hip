@@ -305,11 +305,6 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
   using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
   using I6 = std::integral_constant<int, 6>;
-  // d = 64 (half the MFMAs per step, the same vector work): role 1 forms
-  // D - dP on the MFMAs, from negated V rows and D as the initial
-  // accumulator, which saves a subtraction per score after the hand-over
-  // (below).
-  constexpr bool kNegV = D == 64;
 
   // One product with an operand read row-wise from a tile: acc[t] = init[t]
   // + Σ_c tile rows (32t + l%32, chunk c) x kv[c].
@@ -361,8 +356,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
   f32x16 acc[C::NDT];  // dV^T (role 0) or dK^T (role 1): column = key, rows = d
   char *stg = (char *)(stage + ks * 32 * 64);
   auto store_acc = [&](int bh, int kb) __attribute__((always_inline)) {
-    // At d = 64 role 1 accumulates -dK (its dS carries the sign, below).
-    const float f = role == 0 ? 1.f : (kNegV ? -scale : scale);
+    const float f = role == 0 ? 1.f : scale;
     uint16_t *out = (role == 0 ? dV : dK) + (size_t)bh * N * D;
     const int key0 = kb * C::KB + 32 * ks;
 #pragma unroll
@@ -506,58 +500,22 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
         pipeline(KT{}, I2{}, I4{});
       }
       f32x16 dp[NT];
-      if constexpr (kNegV) {
-        // This block's V rows, negated once (sign bits of both 16-bit
-        // halves) in the block's first step, where they are first read.
-        if (cur.it == block_start(cur.kb)) {
-#pragma unroll
-          for (int c = 0; c < C::NCH; ++c)
-#pragma unroll
-            for (int h = 0; h < 4; ++h) kv[c][h] ^= 0x80008000u;
-        }
-        // E = D - dO V^T: the product accumulated onto D, D of row
-        // 32t + 8i + 4g + j in register 4i + j.
-        f32x16 dinit[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4 dd = vec4(Lb, C::BR, t, i);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dinit[t][4 * i + j] = dd[j];
-          }
-        rows_x_kv(dp, dinit, Os);
-      } else {
-        const f32x16 zero[NT] = {};
-        rows_x_kv(dp, zero, Os);  // dP = dO V^T
-      }
+      const f32x16 zero[NT] = {};
+      rows_x_kv(dp, zero, Os);  // dP = dO V^T
       pipeline(KR{}, I1{}, I6{});
       // The next block's V rows, into the registers the products above read.
       if (last && more) load_rows(nxt);
       barrier_lds();  // the partner's P is in LDS
-      if constexpr (kNegV) {
-        // -dS = P o E = -(P o (dP - D)), rounded to T (rounding commutes
-        // with the sign, so the dK accumulated from it is exactly -dK).
+      // dS = P o (dP - D), rounded to T.
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4 p = *(const f32x4 *)(pxs + ((t * 4 + i) * 64 + lane) * 4);
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 p = *(const f32x4 *)(pxs + ((t * 4 + i) * 64 + lane) * 4);
+          const f32x4 dd = vec4(Lb, C::BR, t, i);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dp[t][4 * i + j] = p[j] * dp[t][4 * i + j];
-          }
-      } else {
-        // dS = P o (dP - D), rounded to T.
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4 p = *(const f32x4 *)(pxs + ((t * 4 + i) * 64 + lane) * 4);
-            const f32x4 dd = vec4(Lb, C::BR, t, i);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dp[t][4 * i + j] = p[j] * (dp[t][4 * i + j] - dd[j]);
-          }
-      }
+          for (int j = 0; j < 4; ++j) dp[t][4 * i + j] = p[j] * (dp[t][4 * i + j] - dd[j]);
+        }
       pack_b(dp, pd);
       __builtin_amdgcn_sched_barrier(0);
       Qprev = Qs;
@@ -577,6 +535,286 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
     tr_x_b(acc, Qprev, pd);  // dK^T += Q^T dS of the last step
     pipeline(KT{}, I2{}, I4{});
     store_acc(prev_bh, prev_kb);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV at d = 64: symmetric waves.
+// ---------------------------------------------------------------------------
+// At d = 64 one wave has room for the K and the V rows of its 32 keys and
+// for both accumulators, so the eight waves split a step by keys and query
+// rows instead of by role: wave w owns key slice w % 4 (32 keys of the
+// block) and query half w / 4 (rows 32h .. 32h + 31 of each 64-row tile),
+// and forms S, P, dP, dS and the dV and dK products of that 32 x 32 piece
+// itself. There is no P hand-over and one barrier per step (the tile
+// rotation); the step's vector work (exponentials, dS) is half a role-0
+// step's. The two waves of a key slice (one SIMD) sum their dV and dK
+// partials once per block through LDS: half 1 writes, half 0 adds them to
+// its own in that fixed order and stores. Loads and stores stay apart: only
+// half-1 waves issue the tile loads and only half-0 waves store, so no wait
+// for tile loads includes a store.
+//
+// The stream of steps, the work units, the tile format in LDS and the
+// operand reads are those of bwd_dkdv_kernel; D - dP is formed on the MFMAs
+// as there at d = 64 (negated V rows, D as the initial accumulator), and
+// dK is accumulated negated.
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv64_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
+    const float *__restrict__ LSE, const float *__restrict__ Dvec, uint16_t *__restrict__ dK,
+    uint16_t *__restrict__ dV, int N, int nkb, int nunits, int total, float c2, float scale) {
+  constexpr int D = 64, KB = 128, BR = 64;
+  constexpr int NCH = D / 16, NDT = D / 32, CPR = D / 8;
+  constexpr int QTILE = BR * D;            // 16-bit elements per Q or dO tile
+  constexpr int LPW = BR * CPR / 256;      // loads per loading wave per tile and tensor
+  constexpr int RED = 2 * NDT * 16 * 64;   // floats of one slice's dV and dK partials
+  // Two buffers (the step's tile, the next one being loaded): Q at
+  // qo + 2*b*QTILE, dO right after it; LSE and D rows at lv + 2*b*BR.
+  __shared__ __attribute__((aligned(1024))) uint16_t qo[2 * 2 * QTILE];
+  __shared__ __attribute__((aligned(256))) float lv[2 * 2 * BR];
+  __shared__ __attribute__((aligned(1024))) float red[4 * RED];
+  __shared__ __attribute__((aligned(1024))) uint16_t stage[4 * 32 * D];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int ks = w & 3;  // key slice: keys 32 ks .. +31 of a block
+  const int hq = w >> 2;  // query half: rows 32 hq .. +31 of a tile
+  const int nq = (N + BR - 1) / BR;
+  const int G = gridDim.x;
+
+  auto block_start = [&](int kb) { return CAUSAL ? kb * KB / BR : 0; };
+  auto unit_pos = [&](int v) {
+    DkdvPos p;
+    p.v = v;
+    const int t = v < total ? xcd_tile(v, total) : 0;
+    p.bh = t / nunits;
+    p.u = t - p.bh * nunits;
+    p.half = 0;
+    p.kb = p.u;
+    p.it = block_start(p.u);
+    return p;
+  };
+  auto advance = [&](DkdvPos p) {
+    if (p.it + 1 < nq) {
+      ++p.it;
+      return p;
+    }
+    if (CAUSAL && p.half == 0 && p.u != nkb - 1 - p.u) {
+      p.half = 1;
+      p.kb = nkb - 1 - p.u;
+      p.it = block_start(p.kb);
+      return p;
+    }
+    return unit_pos(p.v + G);
+  };
+
+  // This slice's K and V rows as B operands: lane l holds key
+  // kb*KB + 32 ks + l%32, 8 consecutive columns 16c + 8g .. per chunk c.
+  // Keys past N read row N - 1 (masked). V is negated at the block's first
+  // step, where the rows are first read.
+  u32x4 kr[NCH], vr[NCH];
+  auto load_rows = [&](const DkdvPos &p) __attribute__((always_inline)) {
+    const int key = min(p.kb * KB + 32 * ks + l32, N - 1);
+    const size_t off = (size_t)p.bh * N * D + (size_t)key * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      kr[c] = ld128(K + off + 16 * c + 8 * g);
+      vr[c] = ld128(V + off + 16 * c + 8 * g);
+    }
+  };
+
+  // Direct loads of step p's query tile into buffer b by the four half-1
+  // waves (r = w & 3), as in bwd_dkdv_kernel; waves r < 2 also load the 64
+  // LSE (r = 0) or D (r = 1) values.
+  const int r4 = w & 3;
+  int gq[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) gq[i] = src_of_chunk<D>((r4 * LPW + i) * 64 + lane);
+  auto issue = [&](int b, const DkdvPos &p) __attribute__((always_inline)) {
+    uint16_t *Qb = qo + 2 * b * QTILE, *Ob = Qb + QTILE;
+    const int q0 = p.it * BR;
+    const int rows = min(N - q0, BR);
+    const size_t base = (size_t)p.bh * N * D + (size_t)q0 * D;
+    const i32x4 qrs = make_rsrc(Q + base, (uint32_t)rows * D * 2);
+    const i32x4 ors = make_rsrc(dO + base, (uint32_t)rows * D * 2);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      dma_lds16(qrs, gq[i], 0, Qb + (r4 * LPW + i) * 512);
+      dma_lds16(ors, gq[i], 0, Ob + (r4 * LPW + i) * 512);
+    }
+    if (r4 < 2) {
+      const i32x4 vrs = make_rsrc((r4 == 0 ? LSE : Dvec) + (size_t)p.bh * N + q0, (uint32_t)rows * 4);
+      dma_lds4(vrs, 4 * lane, 0, lv + 2 * b * BR + r4 * BR);
+    }
+  };
+
+  const int rb = row_base<D>(lane);
+  const int tb1 = tr_base<D>(4 * g, lane), tb2 = tr_base<D>(8 + 4 * g, lane);
+  float *myred = red + ks * RED;
+  uint16_t *stg = stage + ks * 32 * D;
+
+  f32x16 accV[NDT], accK[NDT];  // dV^T and -dK^T / scale: column = key, rows = d
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) accV[dt] = accK[dt] = kZero16;
+
+  DkdvPos cur = unit_pos(blockIdx.x);
+  load_rows(cur);
+  if (hq == 1) issue(0, cur);
+  int b = 0;
+  for (;;) {
+    if (hq == 1) wait_vmem_all();
+    barrier_lds();  // the tile landed; every wave is done with the other buffer
+    const uint16_t *Qs = qo + 2 * b * QTILE + 32 * D * hq;  // this wave's 32 rows
+    const uint16_t *Os = Qs + QTILE;
+    const float *Lb = lv + 2 * b * BR + 32 * hq;
+    const int r0 = cur.it * BR + 32 * hq;  // first query row of this wave
+    const int wk0 = cur.kb * KB + 32 * ks;
+    const int mykey = wk0 + l32;
+    const bool need_mask = (r0 + 32 > N) || (wk0 + 32 > N) || (CAUSAL && wk0 + 31 > r0);
+    const bool last = cur.it == nq - 1;
+    const DkdvPos nxt = advance(cur);
+    const bool more = nxt.v < total;
+    if (hq == 1 && more) issue(b ^ 1, nxt);
+    if (cur.it == block_start(cur.kb)) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) vr[c][h] ^= 0x80008000u;
+    }
+    // LSE and D of rows r0 + 8i + 4g + j (register 4i + j), 16-byte reads.
+    f32x4 lse[4];
+    f32x16 e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lse[i] = *(const f32x4 *)(Lb + 8 * i + 4 * g);
+      const f32x4 dd = *(const f32x4 *)(Lb + BR + 8 * i + 4 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) e[4 * i + j] = dd[j];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      s = mfma32<T>(ld128(at(Qs, rb ^ (32 * c))), kr[c], c == 0 ? kZero16 : s);
+    __builtin_amdgcn_sched_barrier(0);
+    if (need_mask) {
+      // Query r0 + 4g + off sees this lane's key iff lo <= off <= hi.
+      const int hi = (mykey < N ? N - 1 : -1) - r0 - 4 * g;
+      const int lo = CAUSAL ? mykey - r0 - 4 * g : INT_MIN;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        if (off > hi || (CAUSAL && off < lo)) s[r] = -INFINITY;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // E MFMAs beside the exponentials.
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) e = mfma32<T>(ld128(at(Os, rb ^ (32 * c))), vr[c], e);
+    float p[16];
+    u32x4 pp[2], pd[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], c2, -lse[r / 4][r % 4] * kLog2e));
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) pp[cc][h] = pack2<T>(p[8 * cc + 2 * h], p[8 * cc + 2 * h + 1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < NCH - 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // The next block's rows, into the registers the products above read.
+    if (last && more) load_rows(nxt);
+    // dV^T += dO^T P beside -dS = P o E; then -dK^T += Q^T (-dS).
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint16_t *so = Os + 16 * cc * D;
+        accV[dt] = mfma32<T>(
+            cat(ld_tr16(at(so, tb1 ^ (64 * dt))), ld_tr16(at(so, tb2 ^ (64 * dt)))), pp[cc],
+            accV[dt]);
+      }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int r = 8 * cc + 2 * h;
+        pd[cc][h] = pack2<T>(p[r] * e[r], p[r + 1] * e[r + 1]);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NDT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 2 * NDT - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint16_t *sq = Qs + 16 * cc * D;
+        accK[dt] = mfma32<T>(
+            cat(ld_tr16(at(sq, tb1 ^ (64 * dt))), ld_tr16(at(sq, tb2 ^ (64 * dt)))), pd[cc],
+            accK[dt]);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NDT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 2 * NDT - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (last) {
+      // The block's dV and dK: half 1 hands its partials to half 0.
+      if (hq == 1) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f32x4 v, k;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              v[j] = accV[dt][4 * i + j];
+              k[j] = accK[dt][4 * i + j];
+            }
+            *(f32x4 *)(myred + ((0 * NDT + dt) * 4 + i) * 256 + 4 * lane) = v;
+            *(f32x4 *)(myred + ((1 * NDT + dt) * 4 + i) * 256 + 4 * lane) = k;
+          }
+      }
+      barrier_lds();
+      if (hq == 0) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 v = *(const f32x4 *)(myred + ((0 * NDT + dt) * 4 + i) * 256 + 4 * lane);
+            const f32x4 k = *(const f32x4 *)(myred + ((1 * NDT + dt) * 4 + i) * 256 + 4 * lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              accV[dt][4 * i + j] += v[j];
+              accK[dt][4 * i + j] += k[j];
+            }
+          }
+        // The next block's rows are waited for here, before the stores, so
+        // that no later wait includes the stores.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        const size_t o = (size_t)cur.bh * N * D + (size_t)wk0 * D;
+        store_tile_rows<T, D>(accV, 1.f, stg, dV + o, N - wk0, lane);
+        store_tile_rows<T, D>(accK, -scale, stg, dK + o, N - wk0, lane);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) accV[dt] = accK[dt] = kZero16;
+    }
+    if (!more) break;
+    cur = nxt;
+    b ^= 1;
   }
 }
 
@@ -878,9 +1116,14 @@ static hipError_t dkdv(const BwdArgs &a, void *dK, void *dV, hipStream_t st) {
       cus <= 0)
     cus = 256;
   const int grid = min(total, cus);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(C::kThreads), 0, st,
-                     a.Q, a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N, nkb,
-                     nunits, total, a.c2, a.scale);
+  if constexpr (D == 64)
+    hipLaunchKernelGGL((bwd_dkdv64_kernel<T, CAUSAL>), dim3(grid), dim3(512), 0, st, a.Q, a.K, a.V,
+                       a.dO, a.LSE, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N, nkb, nunits,
+                       total, a.c2, a.scale);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(C::kThreads), 0, st,
+                       a.Q, a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N,
+                       nkb, nunits, total, a.c2, a.scale);
   return hipGetLastError();
 }
 
