@@ -196,9 +196,10 @@ __device__ __forceinline__ void buffer_load_lds16(const i32x4 &rsrc, int voffset
 // vector-memory loads complete in issue order, so extra loads it does not
 // know about only make its waits longer. M0 is saved and restored; its write
 // needs one wait state before the load.
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
+// A generic pointer into LDS is the shared aperture's base in the upper 32
+// bits and the LDS byte offset in the lower 32, so truncating it gives the
+// offset (a cast to the LDS address space would add a null-pointer check).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
 __device__ __forceinline__ void dma_lds16(const i32x4 &rsrc, int voffset, uint32_t soffset,
                                           const void *lds_base) {
   uint32_t saved;
