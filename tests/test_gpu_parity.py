@@ -184,6 +184,20 @@ def test_eight_wave_blocks_ragged(fa, oracle_lib, causal, N):
     _compare_slices(oracle_lib, w, inp, got, [(0, 0), (3, 15)], True)
 
 
+@pytest.mark.parametrize("dt,causal", [("bf16", False), ("f16", True)])
+def test_d64_sweep_streams_several_units(fa, oracle_lib, dt, causal):
+    """d = 64 with more key-block units than compute units, so that every
+    workgroup of the dK/dV sweep walks several units (blocks of different
+    slices, the next block's rows and first tile loaded during the previous
+    block's last step), N = 2000 leaving a partial last key block and query
+    tile: corner slices and two others against the oracle."""
+    w = ai.custom("d64-units-%s-%s" % (dt, "c" if causal else "nc"), 4, 16, 2000, 64, dt,
+                  causal, seed=64)
+    inp = ai.make_inputs(w)
+    got = _run(fa, w, inp)
+    _compare_slices(oracle_lib, w, inp, got, _corners_and_random(4, 16, 2, seed=9), True)
+
+
 # ---------------------------------------------------------------------------
 # Score ranges that keep moving the running max
 # ---------------------------------------------------------------------------
