@@ -25,6 +25,10 @@ Prints ONE JSON line. Besides the required keys it carries:
                 N = 2048, 4096, 8192 (B*N = 16384 tokens, 16 heads), causal
                 and not, and for the workloads B4 H32 N2048 d128 bf16 and
                 B1 H16 N8192 d64 fp16 causal.
+  small         the two small workloads, launch-latency-bound: B1 H1 N256 d64
+                fp32 (forward only, against the fp32 MFMA peak) and B2 H8
+                N1024 d64 bf16; medians in microseconds and as TFLOPS (part
+                of the sweep leg).
   splitkv       fa_fwd against fa_fwd_splitkv (the library's split choice) on
                 grids with fewer query blocks than the chip has workgroup
                 slots, and the merge kernel's HBM rate.
@@ -53,6 +57,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOPS (fwd; fwd+bwd) bf16 d=128 N=2k–8k, % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c5_traffic.json")
 
 
@@ -91,7 +96,7 @@ def _step_fns(fa, torch, w, d):
     dq, dk, dv = (torch.empty_like(d["q"]) for _ in range(3))
     dvec = torch.empty((B, H, N), dtype=torch.float32, device=d["q"].device)
     L = fa.lib()
-    code = {torch.bfloat16: fa.BF16, torch.float16: fa.F16}[d["q"].dtype]
+    code = {torch.float32: fa.F32, torch.bfloat16: fa.BF16, torch.float16: fa.F16}[d["q"].dtype]
     P = lambda t: t.data_ptr()
     st = torch.cuda.current_stream().cuda_stream
     c = int(w.causal)
@@ -114,7 +119,8 @@ def _step_fns(fa, torch, w, d):
         ck(L.fa_bwd_dkdv(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(d["do"]),
                          P(lse), P(dvec), w.scale, c, P(dk), P(dv), st))
 
-    return (fwd, dqs, dkdv), {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    fns = (fwd, dqs, dkdv) if w.backward else (fwd,)
+    return fns, {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 
 class ClockSampler:
@@ -247,7 +253,7 @@ def time_workload(fa, torch, w, steps, warmup, per_kernel=True, settle_s=0.0, sa
         if done >= warmup:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    names = ("fwd", "bwd_dq", "bwd_dkdv")
+    names = ("fwd", "bwd_dq", "bwd_dkdv")[:len(fns)]
     # Events between the launches of every step (they sit on the same stream
     # and add no work); the step time is first event to last.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
@@ -693,6 +699,28 @@ def main():
             print("# sweep %s fwd %.1f TFLOPS fwd+bwd %.1f TFLOPS" % (name, ff, tf),
                   file=sys.stderr, flush=True)
         out["sweep"] = sweep
+        # The two small workloads: c1, the fp32 forward (the shape of the
+        # essay's test harness), and c2. One or a few workgroups per launch:
+        # launch latency dominates, so these are latencies, not throughput.
+        small = []
+        for name in ("c1", "c2"):
+            ws = ai.WORKLOADS[name]
+            r = time_workload(fa, torch, ws, 20, 3, per_kernel=False, settle_s=0.2)
+            f_ms = r["ms_fwd_median"]
+            peak = PEAK_F32_TFLOPS if ws.dtype == "f32" else PEAK_BF16_TFLOPS
+            ff = ws.fwd_flops() / (f_ms * 1e-3) / 1e12
+            rec = {"workload": name, "B": ws.B, "H": ws.H, "N": ws.N, "d": ws.d,
+                   "dtype": ws.dtype, "causal": ws.causal, "fwd_us": round(f_ms * 1e3, 2),
+                   "fwd_tflops": round(ff, 2), "fwd_frac": round(ff / peak, 4), "peak": peak}
+            if ws.backward:
+                s_ms = r["ms_step_median"]
+                tf = (ws.fwd_flops() + ws.bwd_flops()) / (s_ms * 1e-3) / 1e12
+                rec.update(fwdbwd_us=round(s_ms * 1e3, 2), fwdbwd_tflops=round(tf, 2),
+                           fwdbwd_frac=round(tf / peak, 4))
+            del r
+            small.append(rec)
+            print("# small %s fwd %.1f us" % (name, rec["fwd_us"]), file=sys.stderr, flush=True)
+        out["small"] = small
     if not args.no_splitkv:
         out["splitkv"] = splitkv_report(fa, torch, min(args.settle, 0.5))
     if not args.no_kvcache:

@@ -612,23 +612,39 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  // The K and V tile of step kt + 1 is loaded into registers while step kt
+  // computes (thread t holds 16-byte pieces e = t, t + 256, ... of it), and
+  // moved into the single LDS buffer once every wave is done with tile kt.
+  constexpr int NL = C::BC * D / 4 / C::kThreads;
+  f32x4 kpre[NL], vpre[NL];
+  auto load_tile = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = tid + i * C::kThreads;
+      const int row = e / (D / 4), col = 4 * (e % (D / 4));
+      const int key = kb + row;
+      kpre[i] = vpre[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (key < N) {
+        kpre[i] = *(const f32x4 *)(Kh + (size_t)key * D + col);
+        vpre[i] = *(const f32x4 *)(Vh + (size_t)key * D + col);
+      }
+    }
+  };
+  if (ntiles > 0) load_tile(0);
   for (int kt = 0; kt < ntiles; ++kt) {
     const int kb = kt * C::BC;
     __syncthreads();
-    for (int e = tid; e < C::BC * D / 4; e += C::kThreads) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = tid + i * C::kThreads;
       const int row = e / (D / 4), col = 4 * (e % (D / 4));
-      const int key = kb + row;
-      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if (key < N) {
-        kv = *(const f32x4 *)(Kh + (size_t)key * D + col);
-        vv = *(const f32x4 *)(Vh + (size_t)key * D + col);
-      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        Ks[row * C::KS + col + u] = kv[u];
-        Vs[row * C::VS + col + u] = vv[u];
+        Ks[row * C::KS + col + u] = kpre[i][u];
+        Vs[row * C::VS + col + u] = vpre[i][u];
       }
     }
+    if (kt + 1 < ntiles) load_tile(kb + C::BC);
     __syncthreads();
     if (CAUSAL && kb > wq0 + 31) continue;
     f32x16 s;
