@@ -797,8 +797,9 @@ __global__ __launch_bounds__(256) void decode_kernel(
   float m = -INFINITY, l = 0.f, o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
-  for (int k0 = kf + w * KPB; k0 < kl; k0 += 4 * KPB) {
-    u32x4 kr[NL], vr[NL];
+  // Batches are double-buffered: the loads of a wave's next batch are issued
+  // before the current one is used, so they stay in flight meanwhile.
+  auto load_batch = [&](int k0, u32x4 (&kr)[NL], u32x4 (&vr)[NL]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       // Keys past the range read its last row again (masked below).
@@ -806,6 +807,9 @@ __global__ __launch_bounds__(256) void decode_kernel(
       kr[i] = ld128(Kh + key * D);
       vr[i] = ld128(Vh + key * D);
     }
+  };
+  auto batch = [&](int k0, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL])
+      __attribute__((always_inline)) {
     float s[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -851,6 +855,22 @@ __global__ __launch_bounds__(256) void decode_kernel(
     for (int off = LPR; off < 64; off <<= 1) ps += __shfl_xor(ps, off);
     l = l * alpha + ps;
     m = mn;
+  };
+  constexpr int kStride = 4 * KPB;  // the four waves take consecutive batches
+  int k0 = kf + w * KPB;
+  if (k0 < kl) {
+    u32x4 ka[NL], va[NL], kb[NL], vb[NL];
+    load_batch(k0, ka, va);
+    for (;;) {
+      if (k0 + kStride < kl) load_batch(k0 + kStride, kb, vb);
+      batch(k0, ka, va);
+      k0 += kStride;
+      if (k0 >= kl) break;
+      if (k0 + kStride < kl) load_batch(k0 + kStride, ka, va);
+      batch(k0, kb, vb);
+      k0 += kStride;
+      if (k0 >= kl) break;
+    }
   }
   // The lane groups share m and l; sum their O, then combine the waves.
 #pragma unroll
