@@ -175,6 +175,44 @@ struct DkdvPos {
   int v, bh, u, half, kb, it;
 };
 
+// The stream itself: blocks of KB keys, query tiles of BR rows, nq tiles per
+// slice, nkb blocks per slice, nunits units per slice, `total` units in all,
+// G workgroups. Under the causal mask a block starts at its first query tile
+// that holds a row at or after its first key.
+template <bool CAUSAL, int KB, int BR>
+struct DkdvStream {
+  int nq, nkb, nunits, total, G;
+  __device__ __forceinline__ int block_start(int kb) const { return CAUSAL ? kb * KB / BR : 0; }
+  // The first step of virtual workgroup v's unit.
+  __device__ __forceinline__ DkdvPos unit_pos(int v) const {
+    DkdvPos p;
+    p.v = v;
+    const int t = v < total ? xcd_tile(v, total) : 0;
+    p.bh = t / nunits;
+    p.u = t - p.bh * nunits;
+    p.half = 0;
+    p.kb = p.u;
+    p.it = block_start(p.u);
+    return p;
+  }
+  // The step after p: the next query tile, the unit's second block, or the
+  // workgroup's next unit (v + G; the stream ends at v >= total).
+  __device__ __forceinline__ DkdvPos advance(DkdvPos p) const {
+    if (p.it + 1 < nq) {
+      ++p.it;
+      return p;
+    }
+    if (CAUSAL && p.half == 0 && p.u != nkb - 1 - p.u) {
+      p.half = 1;
+      p.kb = nkb - 1 - p.u;
+      p.it = block_start(p.kb);
+      return p;
+    }
+    return unit_pos(p.v + G);
+  }
+  __device__ __forceinline__ bool last_of_block(const DkdvPos &p) const { return p.it == nq - 1; }
+};
+
 // Steps of the workgroup's stream. Query-tile buffers rotate over the steps:
 // buffer b (step % 3) holds Q at qo + 2*b*QTILE, dO right after it, and LSE,
 // D rows at lv + 2*b*BR; px is the P hand-over area, PX floats per key slice.
@@ -207,35 +245,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
   const int l32 = lane & 31, g = lane >> 5;
   const int ks = w & 3;     // key slice: keys 32 ks .. +31 of a block
   const int role = w >> 2;  // 0: S, P, dV; 1: dP, dS, dK
-  const int nq = (N + C::BR - 1) / C::BR;
-  const int G = gridDim.x;
-
-  auto block_start = [&](int kb) { return CAUSAL ? kb * C::KB / C::BR : 0; };
-  auto unit_pos = [&](int v) {
-    DkdvPos p;
-    p.v = v;
-    const int t = v < total ? xcd_tile(v, total) : 0;
-    p.bh = t / nunits;
-    p.u = t - p.bh * nunits;
-    p.half = 0;
-    p.kb = p.u;
-    p.it = block_start(p.u);
-    return p;
-  };
-  auto advance = [&](DkdvPos p) {
-    if (p.it + 1 < nq) {
-      ++p.it;
-      return p;
-    }
-    if (CAUSAL && p.half == 0 && p.u != nkb - 1 - p.u) {
-      p.half = 1;
-      p.kb = nkb - 1 - p.u;
-      p.it = block_start(p.kb);
-      return p;
-    }
-    return unit_pos(p.v + G);
-  };
-  auto last_of_block = [&](const DkdvPos &p) { return p.it == nq - 1; };
+  const DkdvStream<CAUSAL, C::KB, C::BR> stream{(N + C::BR - 1) / C::BR, nkb, nunits, total,
+                                                 (int)gridDim.x};
 
   // This slice's K (role 0) or V (role 1) rows as the B operand: lane l
   // holds key kb*KB + 32 ks + l%32, 8 consecutive columns 16c + 8g .. per
@@ -391,7 +402,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
   // before that ended a block (lastA: step n-1, lastB: step n-2), else role 0.
   auto loader = [](bool lastA, bool lastB) { return (lastA || lastB) ? 1 : 0; };
 
-  DkdvPos cur = unit_pos(blockIdx.x);
+  DkdvPos cur = stream.unit_pos(blockIdx.x);
   load_rows(cur);
   if (role == 0) issue(0, cur);
   bool mine = role == 0;     // this wave issued the loads of the current step
@@ -408,8 +419,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
       const int wk0 = cur.kb * C::KB + 32 * ks;  // first key of this wave
       const int mykey = wk0 + l32;               // key of this lane's S/P column
       const bool need_mask = (q0 + C::BR > N) || (wk0 + 32 > N) || (CAUSAL && wk0 + 31 > q0);
-      const bool last = last_of_block(cur);
-      const DkdvPos nxt = advance(cur);
+      const bool last = stream.last_of_block(cur);
+      const DkdvPos nxt = stream.advance(cur);
       const bool more = nxt.v < total;
       const int bn = b == 2 ? 0 : b + 1;
       f32x4 lse[NT][4];
@@ -482,8 +493,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
       barrier_lds();
       const uint16_t *Qs = qo + 2 * b * C::QTILE, *Os = Qs + C::QTILE;
       const float *Lb = lv + 2 * b * C::BR;
-      const bool last = last_of_block(cur);
-      const DkdvPos nxt = advance(cur);
+      const bool last = stream.last_of_block(cur);
+      const DkdvPos nxt = stream.advance(cur);
       const bool more = nxt.v < total;
       const int bn = b == 2 ? 0 : b + 1;
       const bool next_mine = more && loader(last, prev_last) == 1;
@@ -580,34 +591,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv64_kernel(
   const int l32 = lane & 31, g = lane >> 5;
   const int ks = w & 3;  // key slice: keys 32 ks .. +31 of a block
   const int hq = w >> 2;  // query half: rows 32 hq .. +31 of a tile
-  const int nq = (N + BR - 1) / BR;
-  const int G = gridDim.x;
-
-  auto block_start = [&](int kb) { return CAUSAL ? kb * KB / BR : 0; };
-  auto unit_pos = [&](int v) {
-    DkdvPos p;
-    p.v = v;
-    const int t = v < total ? xcd_tile(v, total) : 0;
-    p.bh = t / nunits;
-    p.u = t - p.bh * nunits;
-    p.half = 0;
-    p.kb = p.u;
-    p.it = block_start(p.u);
-    return p;
-  };
-  auto advance = [&](DkdvPos p) {
-    if (p.it + 1 < nq) {
-      ++p.it;
-      return p;
-    }
-    if (CAUSAL && p.half == 0 && p.u != nkb - 1 - p.u) {
-      p.half = 1;
-      p.kb = nkb - 1 - p.u;
-      p.it = block_start(p.kb);
-      return p;
-    }
-    return unit_pos(p.v + G);
-  };
+  const DkdvStream<CAUSAL, KB, BR> stream{(N + BR - 1) / BR, nkb, nunits, total, (int)gridDim.x};
 
   // This slice's K and V rows as B operands: lane l holds key
   // kb*KB + 32 ks + l%32, 8 consecutive columns 16c + 8g .. per chunk c.
@@ -658,7 +642,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv64_kernel(
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) accV[dt] = accK[dt] = kZero16;
 
-  DkdvPos cur = unit_pos(blockIdx.x);
+  DkdvPos cur = stream.unit_pos(blockIdx.x);
   load_rows(cur);
   if (hq == 1) issue(0, cur);
   int b = 0;
@@ -672,11 +656,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv64_kernel(
     const int wk0 = cur.kb * KB + 32 * ks;
     const int mykey = wk0 + l32;
     const bool need_mask = (r0 + 32 > N) || (wk0 + 32 > N) || (CAUSAL && wk0 + 31 > r0);
-    const bool last = cur.it == nq - 1;
-    const DkdvPos nxt = advance(cur);
+    const bool last = stream.last_of_block(cur);
+    const DkdvPos nxt = stream.advance(cur);
     const bool more = nxt.v < total;
     if (hq == 1 && more) issue(b ^ 1, nxt);
-    if (cur.it == block_start(cur.kb)) {
+    if (cur.it == stream.block_start(cur.kb)) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
