@@ -124,7 +124,8 @@ __device__ __forceinline__ int src_of_chunk(int p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: key blocks outer, query tiles inner.
+// dK, dV: key blocks outer, query tiles inner (d = 128; d = 64 runs
+// bwd_dkdv64_kernel below, on the same stream of steps).
 // ---------------------------------------------------------------------------
 template <int D>
 struct DkdvCfg {
@@ -566,9 +567,11 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
 // for tile loads includes a store.
 //
 // The stream of steps, the work units, the tile format in LDS and the
-// operand reads are those of bwd_dkdv_kernel; D - dP is formed on the MFMAs
-// as there at d = 64 (negated V rows, D as the initial accumulator), and
-// dK is accumulated negated.
+// operand reads are those of bwd_dkdv_kernel. D - dP is formed on the MFMAs:
+// the V rows are kept negated and D is the initial accumulator, so the
+// products return E = D - dP, and -dS = P o E costs one multiply per score;
+// dK is accumulated negated (rounding commutes with the sign) and scaled by
+// -scale at the end.
 template <typename T, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv64_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
