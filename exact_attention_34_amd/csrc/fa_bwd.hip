@@ -845,36 +845,6 @@ __device__ __forceinline__ void dq_block(
   const size_t base = (size_t)bh * N * D;
   const uint16_t *Qh = Q + base, *Kh = K + base, *Vh = V + base, *dOh = dO + base;
 
-  // Rows past N are read from row N - 1 (always valid memory) and never
-  // stored.
-  const int qld = min(qrow, N - 1);
-  u32x4 qreg[C::NCH], oreg[C::NCH];
-#pragma unroll
-  for (int c = 0; c < C::NCH; ++c) {
-    qreg[c] = ld128(Qh + (size_t)qld * D + 16 * c + 8 * g);
-    oreg[c] = ld128(dOh + (size_t)qld * D + 16 * c + 8 * g);
-  }
-  const float lse2 = LSE[(size_t)bh * N + qld] * kLog2e;
-  // D of this row: read, or (DFUSE) formed here from O and the dO chunks
-  // already in registers -- lane g holds chunks 2c + g, so the chunk tree of
-  // the preprocess kernel runs within the lane down to the last level, which
-  // joins the lane pair -- and stored for the dK/dV sweep.
-  float dd;
-  if constexpr (DFUSE) {
-    float part[C::NCH];
-#pragma unroll
-    for (int c = 0; c < C::NCH; ++c)
-      part[c] = dot8<T>(ld128(O + base + (size_t)qld * D + 16 * c + 8 * g), oreg[c]);
-#pragma unroll
-    for (int h = C::NCH / 2; h > 0; h >>= 1)
-#pragma unroll
-      for (int c = 0; c < h; ++c) part[c] = part[c] + part[c + h];
-    dd = pair_sum(part[0]);
-    if (qrow < N && g == 0) Dvec[(size_t)bh * N + qrow] = dd;
-  } else {
-    dd = Dvec[(size_t)bh * N + qld];
-  }
-
   const int kend = CAUSAL ? min(N, q0 + C::BR) : N;
   const int ntiles = (kend + C::BC - 1) / C::BC;
 
@@ -906,6 +876,43 @@ __device__ __forceinline__ void dq_block(
       }
     }
   };
+  // Rows past N are read from row N - 1 (always valid memory) and never
+  // stored.
+  const int qld = min(qrow, N - 1);
+  u32x4 qreg[C::NCH], oreg[C::NCH], orow[DFUSE ? C::NCH : 1];
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    qreg[c] = ld128(Qh + (size_t)qld * D + 16 * c + 8 * g);
+    oreg[c] = ld128(dOh + (size_t)qld * D + 16 * c + 8 * g);
+  }
+  const float lse2 = LSE[(size_t)bh * N + qld] * kLog2e;
+  float dd;
+  if constexpr (DFUSE) {
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) orow[c] = ld128(O + base + (size_t)qld * D + 16 * c + 8 * g);
+  } else {
+    dd = Dvec[(size_t)bh * N + qld];
+  }
+  // The first K/V tile goes out with the row loads (one memory round trip
+  // before the first tile), and everything is waited for here with a wait
+  // the compiler sees: its own waits for the rows would otherwise sit inside
+  // the loop, where they would also wait for each next tile.
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // D of this row (DFUSE), formed from O and the dO chunks in registers --
+  // lane g holds chunks 2c + g, so the chunk tree of the preprocess kernel
+  // runs within the lane down to the last level, which joins the lane pair
+  // -- and stored for the dK/dV sweep at the end of the block.
+  if constexpr (DFUSE) {
+    float part[C::NCH];
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) part[c] = dot8<T>(orow[c], oreg[c]);
+#pragma unroll
+    for (int h = C::NCH / 2; h > 0; h >>= 1)
+#pragma unroll
+      for (int c = 0; c < h; ++c) part[c] = part[c] + part[c + h];
+    dd = pair_sum(part[0]);
+  }
 
   const int rb = row_base<D>(lane);
   // K^T operand of dQ^T: keys 16cc + 4g + (0..3) and 16cc + 8 + 4g + (0..3)
@@ -1021,7 +1028,6 @@ __device__ __forceinline__ void dq_block(
     const uint16_t *Ks = kv + 2 * b * C::TILE;
     tile_step(Ks, Ks + C::TILE, kt, diag_tag);
   };
-  issue(0, 0);
   for (int kt = 0; kt < nmain; ++kt) sweep_tile(kt, std::false_type{});
   if constexpr (CAUSAL)
     for (int kt = nmain; kt < ntiles; ++kt) sweep_tile(kt, std::true_type{});
@@ -1032,6 +1038,7 @@ __device__ __forceinline__ void dq_block(
   wait_vmem_all();
   __syncthreads();
   store_tile_rows<T, D>(dq, scale, kv + w * 32 * D, dQ + base + (size_t)wq0 * D, N - wq0, lane);
+  if (DFUSE && qrow < N && g == 0) Dvec[(size_t)bh * N + qrow] = dd;
 }
 
 // Work units as in the forward: one query block, or under the causal mask

@@ -373,6 +373,12 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
       dma(k1rs, gk, K1, i);
     }
   }
+  // The Q rows are used here, so that their loads are in flight with the
+  // tile loads: the compiler may otherwise issue them (loads of a read-only
+  // argument) after the wait below, at their first use, a second memory
+  // round trip before the first tile.
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) asm volatile("" ::"v"(qreg[c]));
   wait_vmem_all();
   __syncthreads();
   if (PART && wq0 >= Nq) {
