@@ -390,7 +390,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
       for (int k = 0; k < 4; ++k) {
         const int r = 8 * k + (lane >> 3), c = lane & 7;
         const u32x4 v = *(const u32x4 *)(stg + r * 128 + 16 * (c ^ (r & 7)));
-        if (key0 + r < N) st128(out + (size_t)(key0 + r) * D + 64 * h + 8 * c, v);
+        if (key0 + r < N) st128_nt(out + (size_t)(key0 + r) * D + 64 * h + 8 * c, v);
       }
     }
 #pragma unroll

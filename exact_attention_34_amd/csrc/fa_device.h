@@ -131,6 +131,12 @@ __device__ __forceinline__ int xcd_tile(int wg, int total) {
 
 __device__ __forceinline__ u32x4 ld128(const void *p) { return *(const u32x4 *)p; }
 __device__ __forceinline__ void st128(void *p, const u32x4 &v) { *(u32x4 *)p = v; }
+// Non-temporal 16-byte store (global_store ... nt), for outputs that no
+// kernel of the pass reads again: they then take less room in L2 from the
+// tiles that other workgroups are still reading.
+__device__ __forceinline__ void st128_nt(void *p, const u32x4 &v) {
+  __builtin_nontemporal_store(v, (u32x4 *)p);
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -280,7 +286,7 @@ __device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[D / 32], flo
   for (int k = 0; k < 32 / RPI; ++k) {
     const int r = RPI * k + lane / CPR, c = lane % CPR;
     const u32x4 v = *(const u32x4 *)(st + r * 2 * D + 16 * (c ^ (r % CPR)));
-    if (r < nrows) *(u32x4 *)(out + (size_t)r * D + 8 * c) = v;
+    if (r < nrows) st128_nt(out + (size_t)r * D + 8 * c, v);
   }
 }
 
