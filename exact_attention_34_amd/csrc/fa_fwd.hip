@@ -717,6 +717,180 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(
   }
 }
 
+// fp32 forward with the keys of a row group split over the waves of one
+// workgroup, for launches too small to fill the GPU with fwd_f32_kernel's
+// 128-row blocks (its waves each sweep every key tile of their rows one
+// after another, a latency of ntiles x 64 fp32 MFMAs). Here a workgroup
+// owns 32 query rows; wave w sweeps key tiles w, w + W, w + 2W, ... of their
+// range with the same per-tile arithmetic as fwd_f32_kernel, in an LDS tile
+// buffer of its own (no barrier inside the sweep), and ends with its own
+// running (m, l, O~). The W partial results of each row are then combined
+// with the two-block merge of the online softmax ("Flash Attention" notes,
+// section 2, parts 3.1 and 4.1) in closed form over the parts:
+//   M = max_w m_w,  L = sum_w l_w 2^(m_w - M),  O = sum_w O~_w 2^(m_w - M) / L,
+// (base-2 units, as m is kept), through LDS. A wave without tiles
+// contributes m = -inf, l = 0, O~ = 0, i.e. weight 0.
+template <int D>
+struct FwdF32KsCfg {
+  static constexpr int W = (D == 64) ? 8 : 4;  // waves (key shares) per workgroup
+  static constexpr int kThreads = 64 * W;
+  static constexpr int BC = 32;                // keys per tile
+  static constexpr int KS = D + 2;             // row strides as in FwdF32Cfg
+  static constexpr int VS = D + 8;
+  static constexpr int NDT = D / 32;
+  static constexpr int TILE = BC * (KS + VS);  // floats of one wave's K and V tile
+  static constexpr int NL = BC * D / 4 / 64;   // 16-byte pieces per lane and tensor
+  static constexpr int TPR = kThreads / 32;    // merge: threads per row
+  static constexpr int CPT = D / TPR;          // merge: columns per thread
+  static_assert(W * 32 * D + 2 * W * 32 <= W * TILE, "the merge reuses the tile buffers");
+  static_assert(CPT % 4 == 0, "whole 16-byte column groups per merge thread");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(FwdF32KsCfg<D>::kThreads, 1) void fwd_f32_ks_kernel(
+    const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
+    float *__restrict__ O, float *__restrict__ LSE, int N, int nrg, int total, float c2) {
+  using C = FwdF32KsCfg<D>;
+  __shared__ __attribute__((aligned(16))) float lds[C::W * C::TILE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int bh = tile / nrg;
+  const int q0 = (tile - bh * nrg) * 32;
+  const int qrow = q0 + l32;
+  const size_t base = (size_t)bh * N * D;
+  const float *Qh = Q + base, *Kh = K + base, *Vh = V + base;
+
+  float qreg[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) qreg[c] = (qrow < N) ? Qh[(size_t)qrow * D + 2 * c + g] : 0.f;
+
+  const int kend = CAUSAL ? min(N, q0 + 32) : N;
+  const int ntiles = (kend + C::BC - 1) / C::BC;
+  float *Ks = lds + w * C::TILE, *Vs = Ks + C::BC * C::KS;
+  f32x16 o[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int kt = w; kt < ntiles; kt += C::W) {
+    const int kb = kt * C::BC;
+    // This wave's tile: lane l holds 16-byte pieces e = l, l + 64, ... (the
+    // wave's own reads of the previous tile precede these writes).
+#pragma unroll
+    for (int i = 0; i < C::NL; ++i) {
+      const int e = lane + 64 * i;
+      const int row = e / (D / 4), col = 4 * (e % (D / 4));
+      const int key = kb + row;
+      f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
+      if (key < N) {
+        kx = *(const f32x4 *)(Kh + (size_t)key * D + col);
+        vx = *(const f32x4 *)(Vh + (size_t)key * D + col);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        Ks[row * C::KS + col + u] = kx[u];
+        Vs[row * C::VS + col + u] = vx[u];
+      }
+    }
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c)
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[l32 * C::KS + 2 * c + g], qreg[c], s, 0, 0, 0);
+    const bool need_mask = (kb + C::BC > N) || (CAUSAL && kb + C::BC - 1 > q0);
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[r] * c2;
+      if (need_mask) {
+        const int key = kb + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (key >= N || (CAUSAL && key > qrow)) x = -INFINITY;
+      }
+      s[r] = x;
+      mloc = fmaxf(mloc, x);
+    }
+    mloc = pair_max(mloc);
+    const float m_new = fmaxf(m_run, mloc);
+    const float mb = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - mb);
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = fast_exp2(s[r] - mb);
+      psum += s[r];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * C::VS + 32 * dt + l32], s[r], o[dt],
+                                                     0, 0, 0);
+      }
+  }
+
+  // The parts, into the tile area once every wave is done with its tiles:
+  // O~_w at Op + (w*32 + row)*D (row-major), m_w and l_w of row r at
+  // Mp[w*32 + r], Lp[w*32 + r].
+  const float l_tot = pair_sum(l_run);
+  __syncthreads();
+  float *Op = lds, *Mp = lds + C::W * 32 * D, *Lp = Mp + C::W * 32;
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(f32x4 *)(Op + (w * 32 + l32) * D + 32 * dt + 8 * i + 4 * g) =
+          f32x4{o[dt][4 * i], o[dt][4 * i + 1], o[dt][4 * i + 2], o[dt][4 * i + 3]};
+  if (g == 0) {
+    Mp[w * 32 + l32] = m_run;
+    Lp[w * 32 + l32] = l_tot;
+  }
+  __syncthreads();
+  // Merge: thread t takes row t / TPR, columns CPT * (t % TPR) .. + CPT - 1.
+  const int row = tid / C::TPR, c0 = C::CPT * (tid % C::TPR);
+  float M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < C::W; ++v) M = fmaxf(M, Mp[v * 32 + row]);
+  const float Mb = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f;
+  f32x4 acc[C::CPT / 4];
+#pragma unroll
+  for (int j = 0; j < C::CPT / 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < C::W; ++v) {
+    const float f = fast_exp2(Mp[v * 32 + row] - Mb);
+    L = __builtin_fmaf(Lp[v * 32 + row], f, L);
+#pragma unroll
+    for (int j = 0; j < C::CPT / 4; ++j) {
+      const f32x4 x = *(const f32x4 *)(Op + (v * 32 + row) * D + c0 + 4 * j);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[j][u] = __builtin_fmaf(x[u], f, acc[j][u]);
+    }
+  }
+  if (q0 + row < N) {
+    const float inv = 1.0f / L;
+    float *Orow = O + base + (size_t)(q0 + row) * D + c0;
+#pragma unroll
+    for (int j = 0; j < C::CPT / 4; ++j)
+      *(f32x4 *)(Orow + 4 * j) =
+          f32x4{acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv};
+    if (c0 == 0) LSE[(size_t)bh * N + q0 + row] = (M + log2f(L)) * kLn2;
+  }
+}
+
 template <typename T, int D, int W, bool CAUSAL>
 static hipError_t fwd_b16_w(int BH, int N, const void *Q, const void *K, const void *V, float c2,
                             void *O, float *LSE, hipStream_t st) {
@@ -743,6 +917,15 @@ static hipError_t fwd_f32(int BH, int N, const void *Q, const void *K, const voi
                           void *O, float *LSE, hipStream_t st) {
   using C = FwdF32Cfg<D>;
   const int nqb = (N + C::BR - 1) / C::BR;
+  if ((long)nqb * BH < kF32SplitBelow) {
+    using S = FwdF32KsCfg<D>;
+    const int nrg = (N + 31) / 32;
+    const int total = nrg * BH;
+    hipLaunchKernelGGL((fwd_f32_ks_kernel<D, CAUSAL>), dim3(total), dim3(S::kThreads), 0, st,
+                       (const float *)Q, (const float *)K, (const float *)V, (float *)O, LSE, N,
+                       nrg, total, c2);
+    return hipGetLastError();
+  }
   const int total = nqb * BH;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(total), dim3(C::kThreads), 0, st,
                      (const float *)Q, (const float *)K, (const float *)V, (float *)O, LSE, N,

@@ -19,6 +19,11 @@ hipError_t launch_fwd(int dtype, int B, int H, int N, int d, const void *Q, cons
 // give every CU one (few slices or short rows), and under the causal mask
 // for N < 4096, where a 256-row block runs more fully masked diagonal tiles
 // than the loads save.
+// fp32 forward: with fewer 128-row blocks than this (half the CUs of an
+// MI355X), each 32-row group runs in one workgroup whose waves split its
+// key tiles and merge their parts (fwd_f32_ks_kernel).
+constexpr long kF32SplitBelow = 128;
+
 inline bool use_256_row_blocks(int BH, int N, bool causal) {
   const int nqb = (N + 255) / 256;
   const long units = (long)BH * (causal ? (nqb + 1) / 2 : nqb);

@@ -93,6 +93,21 @@ def test_small_fwd_f32(fa, oracle_lib, d, causal, N):
     _compare_slices(oracle_lib, w, inp, got, [(0, 0), (0, 1)], False)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", [(1, 2, 1000), (2, 64, 300)])
+def test_fwd_f32_both_paths(fa, oracle_lib, d, causal, B, H, N):
+    """fp32 forward on both sides of the launcher's rule. B1 H2 N1000: 16 blocks
+    of 128 rows, so each 32-row group runs in one workgroup whose waves split its
+    32 key tiles (4 or 8 each) and merge their parts; B2 H64 N300: 384 blocks,
+    one workgroup per 128-row block (fwd_f32_kernel)."""
+    w = ai.Workload("f32-paths-d%d-B%dH%dN%d" % (d, B, H, N), B, H, N, d, "f32", causal, False,
+                    3000 + N + d)
+    inp = ai.make_inputs(w, with_do=False)
+    got = _run(fa, w, inp, backward=False)
+    _compare_slices(oracle_lib, w, inp, got, [(0, 0), (B - 1, H - 1)], False)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_many_tiles_ragged(fa, oracle_lib, causal):
     """N = 1000: 8 query blocks and 16 key tiles, the last ones partial."""
