@@ -762,9 +762,12 @@ __global__ __launch_bounds__(FwdF32KsCfg<D>::kThreads, 1) void fwd_f32_ks_kernel
   const size_t base = (size_t)bh * N * D;
   const float *Qh = Q + base, *Kh = K + base, *Vh = V + base;
 
+  // Rows past N read row N - 1 (finite values, never stored); keys past N
+  // read key N - 1 and are masked (their P is 0): no branch around a load.
   float qreg[D / 2];
+  const float *qsrc = Qh + (size_t)min(qrow, N - 1) * D + g;
 #pragma unroll
-  for (int c = 0; c < D / 2; ++c) qreg[c] = (qrow < N) ? Qh[(size_t)qrow * D + 2 * c + g] : 0.f;
+  for (int c = 0; c < D / 2; ++c) qreg[c] = qsrc[2 * c];
 
   const int kend = CAUSAL ? min(N, q0 + 32) : N;
   const int ntiles = (kend + C::BC - 1) / C::BC;
@@ -784,12 +787,9 @@ __global__ __launch_bounds__(FwdF32KsCfg<D>::kThreads, 1) void fwd_f32_ks_kernel
     for (int i = 0; i < C::NL; ++i) {
       const int e = lane + 64 * i;
       const int row = e / (D / 4), col = 4 * (e % (D / 4));
-      const int key = kb + row;
-      f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-      if (key < N) {
-        kx = *(const f32x4 *)(Kh + (size_t)key * D + col);
-        vx = *(const f32x4 *)(Vh + (size_t)key * D + col);
-      }
+      const int key = min(kb + row, N - 1);
+      const f32x4 kx = *(const f32x4 *)(Kh + (size_t)key * D + col);
+      const f32x4 vx = *(const f32x4 *)(Vh + (size_t)key * D + col);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         Ks[row * C::KS + col + u] = kx[u];
