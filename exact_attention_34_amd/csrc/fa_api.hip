@@ -155,12 +155,13 @@ int check_std(int dtype, int B, int H, int N, int d) {
 }
 size_t std_ds_bytes(int B, int H, int N) { return round_up(std_elems(B, H, N) * 2, kWsAlign); }
 
-// Static scratch of fa_bwd_noalloc: D = rowsum(dO o O) for up to
-// FA_BWD_NOALLOC_MAX_ROWS rows (16 MiB), one copy per device, allocated when
-// the library's code object loads on that device and held until the process
-// ends. Host code never uses this name as an address: the device address of
-// each device's copy comes from hipGetSymbolAddress (scratch_on).
-__device__ __attribute__((aligned(256))) float scratch[FA_BWD_NOALLOC_MAX_ROWS];
+// Static scratch of fa_bwd_noalloc: D = rowsum(dO o O) and LSE * log2(e)
+// for up to FA_BWD_NOALLOC_MAX_ROWS rows each (32 MiB), one copy per device,
+// allocated when the library's code object loads on that device and held
+// until the process ends. Host code never uses this name as an address: the
+// device address of each device's copy comes from hipGetSymbolAddress
+// (scratch_on).
+__device__ __attribute__((aligned(256))) float scratch[2 * FA_BWD_NOALLOC_MAX_ROWS];
 
 constexpr int kMaxDevices = 256;
 std::atomic<float *> g_scratch[kMaxDevices];
@@ -196,16 +197,18 @@ int stream_device(hipStream_t st, int *dev) {
   return FA_OK;
 }
 
-// fa_bwd's two sweeps with D at Dvec (already checked arguments).
+// fa_bwd's two sweeps with D at Dvec and LSE * log2(e) at L2 (already
+// checked arguments).
 int run_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
             const void *O, const void *dO, const float *LSE, float scale, int causal, void *dQ,
-            void *dK, void *dV, float *Dvec, hipStream_t st) {
-  // The dQ sweep forms D itself (as fa_bwd_preprocess would) and stores it
-  // for the dK/dV sweep that follows on the stream.
-  int rc = status(fa::launch_bwd_dq_fused(dtype, B, H, N, d, Q, K, V, O, dO, LSE, Dvec, scale,
-                                          causal, dQ, st));
+            void *dK, void *dV, float *Dvec, float *L2, hipStream_t st) {
+  // The dQ sweep forms D itself (as fa_bwd_preprocess would) and stores it,
+  // with each row's LSE * log2(e), for the dK/dV sweep that follows on the
+  // stream (the same products as the natural-log LSE scaled there).
+  int rc = status(fa::launch_bwd_dq_fused(dtype, B, H, N, d, Q, K, V, O, dO, LSE, Dvec, L2,
+                                          scale, causal, dQ, st));
   if (rc != FA_OK) return rc;
-  return status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
+  return status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, LSE, L2, Dvec, scale, causal,
                                     dK, dV, st));
 }
 
@@ -315,7 +318,7 @@ int fa_fwd_splitkv(int dtype, int B, int H, int N, int d, const void *Q, const v
 
 size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d) {
   if (check_shape(dtype, B, H, N, d, true) != FA_OK) return 0;
-  return d_bytes(B, H, N);
+  return 2 * d_bytes(B, H, N);
 }
 
 int fa_bwd_preprocess(int dtype, int B, int H, int N, int d, const void *O, const void *dO,
@@ -345,8 +348,8 @@ int fa_bwd_dkdv(int dtype, int B, int H, int N, int d, const void *Q, const void
   const int rc = check_sweep(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal);
   if (rc != FA_OK) return rc;
   if (!tensor_ok(dK) || !tensor_ok(dV)) return FA_ERR_INVALID_ARG;
-  return status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal,
-                                    dK, dV, (hipStream_t)stream));
+  return status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, LSE, nullptr, Dvec, scale,
+                                    causal, dK, dV, (hipStream_t)stream));
 }
 
 int fa_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
@@ -365,8 +368,8 @@ int fa_bwd_dq_d(int dtype, int B, int H, int N, int d, const void *Q, const void
   const int rc = check_sweep(dtype, B, H, N, d, Q, K, V, dO, LSE, Dvec, scale, causal);
   if (rc != FA_OK) return rc;
   if (!tensor_ok(O) || !tensor_ok(dQ)) return FA_ERR_INVALID_ARG;
-  return status(fa::launch_bwd_dq_fused(dtype, B, H, N, d, Q, K, V, O, dO, LSE, Dvec, scale,
-                                        causal, dQ, (hipStream_t)stream));
+  return status(fa::launch_bwd_dq_fused(dtype, B, H, N, d, Q, K, V, O, dO, LSE, Dvec, nullptr,
+                                        scale, causal, dQ, (hipStream_t)stream));
 }
 
 int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
@@ -380,8 +383,10 @@ int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, 
       !tensor_ok(workspace))
     return FA_ERR_INVALID_ARG;
   if (workspace_bytes < fa_bwd_workspace_bytes(dtype, B, H, N, d)) return FA_ERR_WORKSPACE;
-  return run_bwd(dtype, B, H, N, d, Q, K, V, O, dO, LSE, scale, causal, dQ, dK, dV,
-                 (float *)workspace, (hipStream_t)stream);
+  float *Dvec = (float *)workspace;
+  float *L2 = (float *)((char *)workspace + d_bytes(B, H, N));
+  return run_bwd(dtype, B, H, N, d, Q, K, V, O, dO, LSE, scale, causal, dQ, dK, dV, Dvec, L2,
+                 (hipStream_t)stream);
 }
 
 int fa_bwd_noalloc(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
@@ -399,9 +404,10 @@ int fa_bwd_noalloc(int dtype, int B, int H, int N, int d, const void *Q, const v
   float *Dvec = nullptr;
   if ((rc = stream_device(st, &dev)) != FA_OK) return rc;
   if ((rc = scratch_on(dev, &Dvec)) != FA_OK) return rc;
-  // Every row of D is written by the dQ sweep before the dK/dV sweep reads
-  // it, so the scratch needs no clearing.
-  return run_bwd(dtype, B, H, N, d, Q, K, V, O, dO, LSE, scale, causal, dQ, dK, dV, Dvec, st);
+  // Every row of D and of LSE * log2(e) is written by the dQ sweep before
+  // the dK/dV sweep reads it, so the scratch needs no clearing.
+  return run_bwd(dtype, B, H, N, d, Q, K, V, O, dO, LSE, scale, causal, dQ, dK, dV, Dvec,
+                 Dvec + FA_BWD_NOALLOC_MAX_ROWS, st);
 }
 
 int fa_std_row_stride(int N) { return N > 0 ? fa::std_row_stride(N) : 0; }

@@ -227,7 +227,11 @@ struct DkdvStream {
 // waits never include store latency. (Vector-memory loads and stores of a
 // wave share one counter and may complete out of order with each other, so
 // a wait for loads alone is only possible when no store is outstanding.)
-template <typename T, int D, bool CAUSAL>
+//
+// L2: LSE holds LSE * log2(e) per row (as the dQ sweep stores it inside
+// fa_bwd), so that P = 2^(S*scale*log2e - L) takes one fma per score;
+// otherwise LSE is the natural-log LSE and is scaled per score.
+template <typename T, int D, bool CAUSAL, bool L2>
 __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
@@ -459,7 +463,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
           f32x4 p;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            p[j] = fast_exp2(__builtin_fmaf(s[t][4 * i + j], c2, -lse[t][i][j] * kLog2e));
+            p[j] = fast_exp2(
+                __builtin_fmaf(s[t][4 * i + j], c2, L2 ? -lse[t][i][j] : -lse[t][i][j] * kLog2e));
           *(f32x4 *)(pxs + ((t * 4 + i) * 64 + lane) * 4) = p;
 #pragma unroll
           for (int j = 0; j < 4; ++j) s[t][4 * i + j] = p[j];
@@ -571,8 +576,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_kernel(
 // the V rows are kept negated and D is the initial accumulator, so the
 // products return E = D - dP, and -dS = P o E costs one multiply per score;
 // dK is accumulated negated (rounding commutes with the sign) and scaled by
-// -scale at the end.
-template <typename T, bool CAUSAL>
+// -scale at the end. LSE as in bwd_dkdv_kernel (L2: already times log2(e)).
+template <typename T, bool CAUSAL, bool L2>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv64_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
@@ -702,7 +707,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv64_kernel(
     float p[16];
     u32x4 pp[2], pd[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], c2, -lse[r / 4][r % 4] * kLog2e));
+    for (int r = 0; r < 16; ++r)
+      p[r] = fast_exp2(
+          __builtin_fmaf(s[r], c2, L2 ? -lse[r / 4][r % 4] : -lse[r / 4][r % 4] * kLog2e));
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
@@ -834,7 +841,8 @@ __device__ __forceinline__ void dq_block(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const uint16_t *__restrict__ O, const float *__restrict__ LSE, float *__restrict__ Dvec,
-    uint16_t *__restrict__ dQ, int N, int bh, int qb, float c2, float scale, uint16_t *kv) {
+    float *__restrict__ L2out, uint16_t *__restrict__ dQ, int N, int bh, int qb, float c2,
+    float scale, uint16_t *kv) {
   using C = DqCfg<D, W>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1038,7 +1046,10 @@ __device__ __forceinline__ void dq_block(
   wait_vmem_all();
   __syncthreads();
   store_tile_rows<T, D>(dq, scale, kv + w * 32 * D, dQ + base + (size_t)wq0 * D, N - wq0, lane);
-  if (DFUSE && qrow < N && g == 0) Dvec[(size_t)bh * N + qrow] = dd;
+  if (DFUSE && qrow < N && g == 0) {
+    Dvec[(size_t)bh * N + qrow] = dd;
+    if (L2out != nullptr) L2out[(size_t)bh * N + qrow] = lse2;
+  }
 }
 
 // Work units as in the forward: one query block, or under the causal mask
@@ -1048,21 +1059,24 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const uint16_t *__restrict__ O, const float *__restrict__ LSE, float *__restrict__ Dvec,
-    uint16_t *__restrict__ dQ, int N, int nqb, int nunits, int total, float c2, float scale) {
+    float *__restrict__ L2out, uint16_t *__restrict__ dQ, int N, int nqb, int nunits, int total,
+    float c2, float scale) {
   using C = DqCfg<D, W>;
   __shared__ __attribute__((aligned(1024))) uint16_t kv[4 * C::TILE];
   const int tile = xcd_tile(blockIdx.x, total);
   const int bh = tile / nunits;
   const int u = tile - bh * nunits;
   if (!CAUSAL) {
-    dq_block<T, D, W, CAUSAL, DFUSE>(Q, K, V, dO, O, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
+    dq_block<T, D, W, CAUSAL, DFUSE>(Q, K, V, dO, O, LSE, Dvec, L2out, dQ, N, bh, u, c2, scale,
+                                     kv);
     return;
   }
-  dq_block<T, D, W, CAUSAL, DFUSE>(Q, K, V, dO, O, LSE, Dvec, dQ, N, bh, nqb - 1 - u, c2, scale,
-                                   kv);
+  dq_block<T, D, W, CAUSAL, DFUSE>(Q, K, V, dO, O, LSE, Dvec, L2out, dQ, N, bh, nqb - 1 - u, c2,
+                                   scale, kv);
   if (u != nqb - 1 - u) {
     __syncthreads();  // every wave is done with the LDS tiles
-    dq_block<T, D, W, CAUSAL, DFUSE>(Q, K, V, dO, O, LSE, Dvec, dQ, N, bh, u, c2, scale, kv);
+    dq_block<T, D, W, CAUSAL, DFUSE>(Q, K, V, dO, O, LSE, Dvec, L2out, dQ, N, bh, u, c2, scale,
+                                     kv);
   }
 }
 
@@ -1094,6 +1108,8 @@ struct BwdArgs {
   float c2, scale;
   const uint16_t *O;  // dQ sweep only: form D from O and dO (else null)
   float *Dout;        // where that sweep writes D (else Dvec, read-only)
+  float *L2out;       // dQ sweep with O: also writes LSE * log2(e) there (or null)
+  const float *L2;    // dK/dV sweep: LSE * log2(e) to read instead of LSE (or null)
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -1110,14 +1126,26 @@ static hipError_t dkdv(const BwdArgs &a, void *dK, void *dV, hipStream_t st) {
       cus <= 0)
     cus = 256;
   const int grid = min(total, cus);
-  if constexpr (D == 64)
-    hipLaunchKernelGGL((bwd_dkdv64_kernel<T, CAUSAL>), dim3(grid), dim3(512), 0, st, a.Q, a.K, a.V,
-                       a.dO, a.LSE, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N, nkb, nunits,
-                       total, a.c2, a.scale);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(C::kThreads), 0, st,
-                       a.Q, a.K, a.V, a.dO, a.LSE, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N,
-                       nkb, nunits, total, a.c2, a.scale);
+  const float *L = a.L2 != nullptr ? a.L2 : a.LSE;
+  if constexpr (D == 64) {
+    if (a.L2 != nullptr)
+      hipLaunchKernelGGL((bwd_dkdv64_kernel<T, CAUSAL, true>), dim3(grid), dim3(512), 0, st, a.Q,
+                         a.K, a.V, a.dO, L, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N, nkb,
+                         nunits, total, a.c2, a.scale);
+    else
+      hipLaunchKernelGGL((bwd_dkdv64_kernel<T, CAUSAL, false>), dim3(grid), dim3(512), 0, st, a.Q,
+                         a.K, a.V, a.dO, L, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N, nkb,
+                         nunits, total, a.c2, a.scale);
+  } else {
+    if (a.L2 != nullptr)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, true>), dim3(grid), dim3(C::kThreads), 0,
+                         st, a.Q, a.K, a.V, a.dO, L, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N,
+                         nkb, nunits, total, a.c2, a.scale);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, false>), dim3(grid), dim3(C::kThreads), 0,
+                         st, a.Q, a.K, a.V, a.dO, L, a.Dvec, (uint16_t *)dK, (uint16_t *)dV, a.N,
+                         nkb, nunits, total, a.c2, a.scale);
+  }
   return hipGetLastError();
 }
 
@@ -1128,7 +1156,7 @@ static hipError_t dq_w(const BwdArgs &a, void *dQ, hipStream_t st) {
   const int nunits = CAUSAL ? (nqb + 1) / 2 : nqb;
   const int total = nunits * a.BH;
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, W, CAUSAL, DFUSE>), dim3(total), dim3(C::kThreads), 0,
-                     st, a.Q, a.K, a.V, a.dO, a.O, a.LSE, a.Dout, (uint16_t *)dQ, a.N, nqb,
+                     st, a.Q, a.K, a.V, a.dO, a.O, a.LSE, a.Dout, a.L2out, (uint16_t *)dQ, a.N, nqb,
                      nunits, total, a.c2, a.scale);
   return hipGetLastError();
 }
@@ -1147,7 +1175,7 @@ static BwdArgs bwd_args(int B, int H, int N, const void *Q, const void *K, const
                         const void *dO, const float *LSE, const float *Dvec, float scale) {
   return BwdArgs{B * H, N, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
                  (const uint16_t *)dO, LSE, Dvec, scale * kLog2e, scale, nullptr,
-                 const_cast<float *>(Dvec)};
+                 const_cast<float *>(Dvec), nullptr, nullptr};
 }
 
 // Instantiates F<T, D, CAUSAL>(args...) for the run-time dtype, d, causal.
@@ -1163,9 +1191,11 @@ static BwdArgs bwd_args(int B, int H, int N, const void *Q, const void *K, const
                                 : F<F16, 128, false>(__VA_ARGS__))))
 
 hipError_t launch_bwd_dkdv(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
-                           const void *V, const void *dO, const float *LSE, const float *Dvec,
-                           float scale, int causal, void *dK, void *dV, hipStream_t st) {
-  const BwdArgs a = bwd_args(B, H, N, Q, K, V, dO, LSE, Dvec, scale);
+                           const void *V, const void *dO, const float *LSE, const float *LSE2,
+                           const float *Dvec, float scale, int causal, void *dK, void *dV,
+                           hipStream_t st) {
+  BwdArgs a = bwd_args(B, H, N, Q, K, V, dO, LSE, Dvec, scale);
+  a.L2 = LSE2;
   return FA_DISPATCH(dkdv, dtype, d, causal, a, dK, dV, st);
 }
 
@@ -1178,11 +1208,12 @@ hipError_t launch_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q, c
 
 hipError_t launch_bwd_dq_fused(int dtype, int B, int H, int N, int d, const void *Q,
                                const void *K, const void *V, const void *O, const void *dO,
-                               const float *LSE, float *Dvec, float scale, int causal, void *dQ,
-                               hipStream_t st) {
+                               const float *LSE, float *Dvec, float *LSE2, float scale,
+                               int causal, void *dQ, hipStream_t st) {
   BwdArgs a = bwd_args(B, H, N, Q, K, V, dO, LSE, Dvec, scale);
   a.O = (const uint16_t *)O;
   a.Dout = Dvec;
+  a.L2out = LSE2;
   return FA_DISPATCH(dq, dtype, d, causal, a, dQ, st);
 }
 

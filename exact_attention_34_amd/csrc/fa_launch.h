@@ -59,10 +59,12 @@ hipError_t launch_lse_merge(int dtype, int parts, long rows, int d, const float 
 hipError_t launch_bwd_preprocess(int dtype, int B, int H, int N, int d, const void *O,
                                  const void *dO, float *Dvec, hipStream_t stream);
 
-// dK, dV (key blocks outer).
+// dK, dV (key blocks outer). LSE2, if not null, holds LSE * log2(e) per row
+// (as launch_bwd_dq_fused writes it) and is read instead of LSE.
 hipError_t launch_bwd_dkdv(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
-                           const void *V, const void *dO, const float *LSE, const float *Dvec,
-                           float scale, int causal, void *dK, void *dV, hipStream_t stream);
+                           const void *V, const void *dO, const float *LSE, const float *LSE2,
+                           const float *Dvec, float scale, int causal, void *dK, void *dV,
+                           hipStream_t stream);
 
 // dQ (query blocks outer).
 hipError_t launch_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
@@ -71,10 +73,11 @@ hipError_t launch_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q, c
 
 // dQ as launch_bwd_dq, with D formed from O and dO inside the sweep (the
 // same values launch_bwd_preprocess computes, bit for bit) and written to
-// Dvec for a dK/dV sweep launched after it.
+// Dvec for a dK/dV sweep launched after it; if LSE2 is not null, the sweep
+// also writes LSE * log2(e) there, the form that sweep's exponentials use.
 hipError_t launch_bwd_dq_fused(int dtype, int B, int H, int N, int d, const void *Q,
                                const void *K, const void *V, const void *O, const void *dO,
-                               const float *LSE, float *Dvec, float scale, int causal, void *dQ,
-                               hipStream_t stream);
+                               const float *LSE, float *Dvec, float *LSE2, float scale,
+                               int causal, void *dQ, hipStream_t stream);
 
 }  // namespace fa

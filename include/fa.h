@@ -184,8 +184,9 @@ int fa_lse_merge(int dtype, int parts, long long rows, int d,
                  float *LSE, void *stream);
 
 /*
- * Bytes of workspace fa_bwd needs: fp32 D [B, H, N], rounded up to a
- * multiple of 256. Returns 0 for arguments fa_bwd would reject.
+ * Bytes of workspace fa_bwd needs: fp32 D [B, H, N] and fp32 LSE * log2(e)
+ * [B, H, N], each rounded up to a multiple of 256. Returns 0 for arguments
+ * fa_bwd would reject.
  */
 size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d);
 
@@ -208,7 +209,9 @@ size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d);
  * fp32. Deterministic: the same inputs give bit-identical dQ, dK and dV
  * (every output element is summed by one thread in a fixed order).
  * Enqueues fa_bwd_dq_d (the dQ sweep, which also forms D into the
- * workspace) and then fa_bwd_dkdv; the results equal fa_bwd_preprocess,
+ * workspace and stores each row's LSE * log2(e) beside it) and then
+ * fa_bwd_dkdv (reading that scaled LSE, the factor its base-2 exponentials
+ * would otherwise apply per score); the results equal fa_bwd_preprocess,
  * fa_bwd_dkdv and fa_bwd_dq called in turn, bit for bit.
  */
 int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
@@ -220,9 +223,10 @@ int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
  * fa_bwd without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc). Same inputs, outputs, kernels and
- * results as fa_bwd (bit for bit). The fp32 D = rowsum(dO o O) that fa_bwd
- * keeps in the caller's workspace lives instead in a static device array of
- * the library, FA_BWD_NOALLOC_MAX_ROWS floats (16 MiB), one copy per device,
+ * results as fa_bwd (bit for bit). The fp32 D = rowsum(dO o O) and
+ * LSE * log2(e) rows that fa_bwd keeps in the caller's workspace live instead
+ * in a static device array of the library, 2 * FA_BWD_NOALLOC_MAX_ROWS floats
+ * (32 MiB), one copy per device,
  * allocated when the library's code loads on that device and held until the
  * process ends; its address is looked up on the first call on each device
  * (the device of `stream`; the current device for the null stream).

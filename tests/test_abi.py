@@ -144,9 +144,9 @@ def test_stage_entry_points_reject(L):
                                           (2, 16, 32, 2048, 128),
                                           (2, 41, 400, 1024, 128)])  # tensors past 4 GiB
 def test_workspace_bytes(L, dtype, B, H, N, d):
-    """fp32 D [B,H,N] rounded up to 256 bytes."""
+    """fp32 D [B,H,N] and fp32 LSE * log2(e) [B,H,N], each rounded up to 256 bytes."""
     dbytes = -(-B * H * N * 4 // 256) * 256
-    assert L.fa_bwd_workspace_bytes(dtype, B, H, N, d) == dbytes
+    assert L.fa_bwd_workspace_bytes(dtype, B, H, N, d) == 2 * dbytes
     assert L.fa_bwd_workspace_bytes(0, B, H, N, d) == 0     # fp32: no backward
     assert L.fa_bwd_workspace_bytes(dtype, B, H, N, 80) == 0
     assert L.fa_bwd_workspace_bytes(dtype, 1 << 16, 1 << 15, 1, d) == 0  # 2^31 rows
