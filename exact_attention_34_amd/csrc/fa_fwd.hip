@@ -381,10 +381,29 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
   for (int c = 0; c < C::NCH; ++c) asm volatile("" ::"v"(qreg[c]));
   wait_vmem_all();
   __syncthreads();
-  if (PART && wq0 >= Nq) {
-    // None of this wave's rows exists (few queries, as in decoding): it only
-    // issues its share of the tile loads and meets every barrier.
-    for (int kt = 0; kt < ntiles; ++kt) {
+  // Tiles this wave computes: under the causal mask the last tiles of a
+  // block can lie wholly after the wave's rows (P = 0 there), and a wave
+  // none of whose rows exists (few queries, as in decoding) computes none.
+  int nmine = ntiles;
+  if (CAUSAL) nmine = min(ntiles, max(qoff + wq0 + 32 - kfirst + C::BC - 1, 0) / C::BC);
+  if (PART && wq0 >= Nq) nmine = 0;
+  if (nmine > 0) {
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) s_mfma(sa, kbuf(0), c);
+    step(std::true_type{}, 0, sa, sb, pb, pa, 0);
+    // Steps 1 .. nmine; step nmine only finishes the P V MFMAs of the
+    // wave's last tile (its own tile is past the wave's keys: P = 0).
+    for (int kt = 1;; kt += 2) {
+      step(std::false_type{}, kt, sb, sa, pa, pb, 1);
+      if (kt >= nmine) break;
+      step(std::false_type{}, kt + 1, sa, sb, pb, pa, 0);
+      if (kt + 1 >= nmine) break;
+    }
+  }
+  // The block's remaining steps (up to step ntiles): the wave only issues
+  // its share of their tile loads and meets their barriers.
+  if (ntiles > 0)
+    for (int kt = nmine > 0 ? nmine + 1 : 0; kt <= ntiles; ++kt) {
       const int b = kt & 1;
       wait_vmem_all();
       __syncthreads();
@@ -395,25 +414,6 @@ __device__ __forceinline__ void fwd_block(const uint16_t *__restrict__ Q,
         dma(vrs, gv, vbuf(b), i);
       }
     }
-    if (ntiles > 0) {
-      wait_vmem_all();
-      __syncthreads();
-    }
-    return;
-  }
-  if (ntiles > 0) {
-#pragma unroll
-    for (int c = 0; c < C::NCH; ++c) s_mfma(sa, kbuf(0), c);
-    step(std::true_type{}, 0, sa, sb, pb, pa, 0);
-    // Steps 1 .. ntiles; step ntiles only finishes the P V MFMAs of the
-    // last tile (its own tile lies past the range: fully masked, P = 0).
-    for (int kt = 1;; kt += 2) {
-      step(std::false_type{}, kt, sb, sa, pa, pb, 1);
-      if (kt >= ntiles) break;
-      step(std::false_type{}, kt + 1, sa, sb, pb, pa, 0);
-      if (kt + 1 >= ntiles) break;
-    }
-  }
   // Epilogue: O = O~ / l, LSE = (m + log2 l) * ln 2.
   const float l_tot = pair_sum(l_run);
   const float inv = fast_rcp(l_tot);
