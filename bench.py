@@ -1,8 +1,9 @@
 """Throughput benchmark: exact attention forward + backward on one MI355X.
 
 One step is one pass of the whole path over one batch: fa_fwd (O, LSE), then
-fa_bwd's two stages as it issues them (the dQ sweep over query blocks, which
-also forms D = rowsum(dO o O), then the dK/dV sweep over key blocks). The workload is the Llama-2-7B-shaped causal attention layer
+fa_bwd as its two launches, called apart (fa_bwd_dq_ws: the dQ sweep over
+query blocks, which also forms D = rowsum(dO o O); fa_bwd_dkdv_ws: the dK/dV
+sweep over key blocks). The workload is the Llama-2-7B-shaped causal attention layer
 (batch 16, 32 heads, N = 2048, d = 128, bf16; rotary Q/K, dO ~ N(0, 0.01)),
 with inputs resident in device memory before the timed region.
 
@@ -94,9 +95,10 @@ def _step_fns(fa, torch, w, d):
     o = torch.empty_like(d["q"])
     lse = torch.empty((B, H, N), dtype=torch.float32, device=d["q"].device)
     dq, dk, dv = (torch.empty_like(d["q"]) for _ in range(3))
-    dvec = torch.empty((B, H, N), dtype=torch.float32, device=d["q"].device)
     L = fa.lib()
     code = {torch.float32: fa.F32, torch.bfloat16: fa.BF16, torch.float16: fa.F16}[d["q"].dtype]
+    ws_bytes = L.fa_bwd_workspace_bytes(code, B, H, N, D) if w.backward else 0
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=d["q"].device)
     P = lambda t: t.data_ptr()
     st = torch.cuda.current_stream().cuda_stream
     c = int(w.causal)
@@ -109,15 +111,17 @@ def _step_fns(fa, torch, w, d):
         ck(L.fa_fwd(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), w.scale, c, P(o),
                     P(lse), st))
 
-    # fa_bwd's own sequence, one ABI call per sweep so that each can be timed:
-    # the dQ sweep (which also forms D = rowsum(dO o O)), then dK/dV.
+    # fa_bwd as its two launches, one ABI call each so that each can be
+    # timed (the same kernels, arguments and results as one fa_bwd call): the
+    # dQ sweep, which also forms D = rowsum(dO o O) and LSE * log2(e) into the
+    # workspace, then the dK/dV sweep, which reads them.
     def dqs():
-        ck(L.fa_bwd_dq_d(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(o), P(d["do"]),
-                         P(lse), P(dvec), w.scale, c, P(dq), st))
+        ck(L.fa_bwd_dq_ws(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(o), P(d["do"]),
+                          P(lse), w.scale, c, P(dq), P(ws), ws_bytes, st))
 
     def dkdv():
-        ck(L.fa_bwd_dkdv(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(d["do"]),
-                         P(lse), P(dvec), w.scale, c, P(dk), P(dv), st))
+        ck(L.fa_bwd_dkdv_ws(code, B, H, N, D, P(d["q"]), P(d["k"]), P(d["v"]), P(d["do"]),
+                            w.scale, c, P(dk), P(dv), P(ws), ws_bytes, st))
 
     fns = (fwd, dqs, dkdv) if w.backward else (fwd,)
     return fns, {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}

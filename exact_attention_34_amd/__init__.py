@@ -14,8 +14,9 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_splitkv", "fwd_splitkv_parts", "fwd_splitkv_workspace_bytes",
-           "fwd_kvcache", "fwd_kvcache_parts", "fwd_kvcache_workspace_bytes", "lse_merge", "bwd", "bwd_noalloc", "bwd_preprocess", "bwd_dkdv", "bwd_dq",
-           "bwd_workspace_bytes", "FAError", "library_path", "lib",
+           "fwd_kvcache", "fwd_kvcache_parts", "fwd_kvcache_workspace_bytes", "lse_merge",
+           "bwd", "bwd_dq_ws", "bwd_dkdv_ws", "bwd_noalloc", "bwd_preprocess", "bwd_dkdv",
+           "bwd_dq", "bwd_dq_d", "bwd_workspace_bytes", "FAError", "library_path", "lib",
            "F32", "F16", "BF16"]
 
 F32, F16, BF16 = 0, 1, 2
@@ -70,6 +71,10 @@ def lib():
     L.fa_bwd_workspace_bytes.restype = z
     L.fa_bwd.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, p, p, z, p]
     L.fa_bwd.restype = i
+    L.fa_bwd_dq_ws.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, z, p]
+    L.fa_bwd_dq_ws.restype = i
+    L.fa_bwd_dkdv_ws.argtypes = [i, i, i, i, i, p, p, p, p, f, i, p, p, p, z, p]
+    L.fa_bwd_dkdv_ws.restype = i
     L.fa_bwd_noalloc.argtypes = [i, i, i, i, i, p, p, p, p, p, p, f, i, p, p, p, p]
     L.fa_bwd_noalloc.restype = i
     L.fa_bwd_preprocess.argtypes = [i, i, i, i, i, p, p, p, p]
@@ -252,6 +257,31 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None):
           _ptr(lse), _scale(scale, d), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
     return dq, dk, dv
+
+
+def bwd_dq_ws(q, k, v, o, do, lse, dq, workspace, scale=None, causal=False):
+    """The first launch of bwd: dQ, with D and the scaled LSE written into
+    `workspace` (a bwd_workspace_bytes() buffer) for bwd_dkdv_ws."""
+    dt, B, H, N, d = _check_qkv(q, k, v, o, do, dq)
+    _check_rows(lse, "lse", q)
+    if workspace is None:
+        raise ValueError("bwd_dq_ws needs the workspace that bwd_dkdv_ws will read")
+    workspace = _workspace(workspace, bwd_workspace_bytes(q.dtype, B, H, N, d), q)
+    _call("fa_bwd_dq_ws", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+          _ptr(lse), _scale(scale, d), int(bool(causal)), _ptr(dq), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(q))
+
+
+def bwd_dkdv_ws(q, k, v, do, dk, dv, workspace, scale=None, causal=False):
+    """The second launch of bwd: dK and dV, reading what bwd_dq_ws wrote into
+    `workspace` for the same inputs."""
+    dt, B, H, N, d = _check_qkv(q, k, v, do, dk, dv)
+    if workspace is None:
+        raise ValueError("bwd_dkdv_ws reads the workspace that bwd_dq_ws wrote")
+    workspace = _workspace(workspace, bwd_workspace_bytes(q.dtype, B, H, N, d), q)
+    _call("fa_bwd_dkdv_ws", dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do),
+          _scale(scale, d), int(bool(causal)), _ptr(dk), _ptr(dv), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(q))
 
 
 def bwd_noalloc(q, k, v, o, do, lse, scale=None, causal=False, out=None):

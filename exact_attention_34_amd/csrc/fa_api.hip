@@ -199,17 +199,29 @@ int stream_device(hipStream_t st, int *dev) {
 
 // fa_bwd's two sweeps with D at Dvec and LSE * log2(e) at L2 (already
 // checked arguments).
+// The two launches of the backward. The dQ sweep forms D itself (as
+// fa_bwd_preprocess would) and stores it, with each row's LSE * log2(e), for
+// the dK/dV sweep that follows (the same products as the natural-log LSE
+// scaled there), which reads both.
+int run_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+               const void *V, const void *O, const void *dO, const float *LSE, float scale,
+               int causal, void *dQ, float *Dvec, float *L2, hipStream_t st) {
+  return status(fa::launch_bwd_dq_fused(dtype, B, H, N, d, Q, K, V, O, dO, LSE, Dvec, L2, scale,
+                                        causal, dQ, st));
+}
+int run_bwd_dkdv(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                 const void *V, const void *dO, float scale, int causal, void *dK, void *dV,
+                 const float *Dvec, const float *L2, hipStream_t st) {
+  // LSE itself is not read when L2 is given.
+  return status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, nullptr, L2, Dvec, scale,
+                                    causal, dK, dV, st));
+}
 int run_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, const void *V,
             const void *O, const void *dO, const float *LSE, float scale, int causal, void *dQ,
             void *dK, void *dV, float *Dvec, float *L2, hipStream_t st) {
-  // The dQ sweep forms D itself (as fa_bwd_preprocess would) and stores it,
-  // with each row's LSE * log2(e), for the dK/dV sweep that follows on the
-  // stream (the same products as the natural-log LSE scaled there).
-  int rc = status(fa::launch_bwd_dq_fused(dtype, B, H, N, d, Q, K, V, O, dO, LSE, Dvec, L2,
-                                          scale, causal, dQ, st));
+  int rc = run_bwd_dq(dtype, B, H, N, d, Q, K, V, O, dO, LSE, scale, causal, dQ, Dvec, L2, st);
   if (rc != FA_OK) return rc;
-  return status(fa::launch_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, LSE, L2, Dvec, scale, causal,
-                                    dK, dV, st));
+  return run_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, scale, causal, dK, dV, Dvec, L2, st);
 }
 
 }  // namespace
@@ -387,6 +399,38 @@ int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K, 
   float *L2 = (float *)((char *)workspace + d_bytes(B, H, N));
   return run_bwd(dtype, B, H, N, d, Q, K, V, O, dO, LSE, scale, causal, dQ, dK, dV, Dvec, L2,
                  (hipStream_t)stream);
+}
+
+int fa_bwd_dq_ws(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                 const void *V, const void *O, const void *dO, const float *LSE, float scale,
+                 int causal, void *dQ, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shape(dtype, B, H, N, d, true);
+  if (rc != FA_OK) return rc;
+  if ((rc = check_scale_causal(scale, causal)) != FA_OK) return rc;
+  if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O) || !tensor_ok(dO) ||
+      !vec_ok(LSE) || !tensor_ok(dQ) || !tensor_ok(workspace))
+    return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_bwd_workspace_bytes(dtype, B, H, N, d)) return FA_ERR_WORKSPACE;
+  float *Dvec = (float *)workspace;
+  float *L2 = (float *)((char *)workspace + d_bytes(B, H, N));
+  return run_bwd_dq(dtype, B, H, N, d, Q, K, V, O, dO, LSE, scale, causal, dQ, Dvec, L2,
+                    (hipStream_t)stream);
+}
+
+int fa_bwd_dkdv_ws(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
+                   const void *V, const void *dO, float scale, int causal, void *dK, void *dV,
+                   const void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shape(dtype, B, H, N, d, true);
+  if (rc != FA_OK) return rc;
+  if ((rc = check_scale_causal(scale, causal)) != FA_OK) return rc;
+  if (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(dO) || !tensor_ok(dK) ||
+      !tensor_ok(dV) || !tensor_ok(workspace))
+    return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_bwd_workspace_bytes(dtype, B, H, N, d)) return FA_ERR_WORKSPACE;
+  const float *Dvec = (const float *)workspace;
+  const float *L2 = (const float *)((const char *)workspace + d_bytes(B, H, N));
+  return run_bwd_dkdv(dtype, B, H, N, d, Q, K, V, dO, scale, causal, dK, dV, Dvec, L2,
+                      (hipStream_t)stream);
 }
 
 int fa_bwd_noalloc(int dtype, int B, int H, int N, int d, const void *Q, const void *K,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 /* element types */
 #define FA_F32 0
@@ -208,16 +208,44 @@ size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d);
  * are rounded to dtype before the products that consume them; all sums are
  * fp32. Deterministic: the same inputs give bit-identical dQ, dK and dV
  * (every output element is summed by one thread in a fixed order).
- * Enqueues fa_bwd_dq_d (the dQ sweep, which also forms D into the
+ * Enqueues fa_bwd_dq_ws (the dQ sweep, which also forms D into the
  * workspace and stores each row's LSE * log2(e) beside it) and then
- * fa_bwd_dkdv (reading that scaled LSE, the factor its base-2 exponentials
- * would otherwise apply per score); the results equal fa_bwd_preprocess,
- * fa_bwd_dkdv and fa_bwd_dq called in turn, bit for bit.
+ * fa_bwd_dkdv_ws (the dK/dV sweep, reading that scaled LSE, the factor its
+ * base-2 exponentials would otherwise apply per score); the results equal
+ * fa_bwd_preprocess, fa_bwd_dkdv and fa_bwd_dq called in turn, bit for bit.
  */
 int fa_bwd(int dtype, int B, int H, int N, int d, const void *Q, const void *K,
            const void *V, const void *O, const void *dO, const float *LSE,
            float scale, int causal, void *dQ, void *dK, void *dV,
            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The two launches of fa_bwd as two calls, for callers that time or
+ * schedule them apart: fa_bwd_dq_ws and then fa_bwd_dkdv_ws, on one
+ * workspace and one stream (or with the first complete before the second
+ * starts), enqueue exactly what fa_bwd enqueues and give the same dQ, dK
+ * and dV, bit for bit.
+ *
+ * fa_bwd_dq_ws: dQ (the dQ sweep of fa_bwd_dq_d); it also writes D =
+ *   rowsum(dO o O) ([FA] derivation page, part 5) and LSE * log2(e) of every
+ *   row into the workspace.
+ *   In: Q, K, V, O, dO dtype; LSE fp32.  Out: dQ dtype; the workspace.
+ * fa_bwd_dkdv_ws: dK, dV (the dK/dV sweep of fa_bwd_dkdv), reading D and
+ *   the scaled LSE that fa_bwd_dq_ws wrote into the workspace for the same
+ *   Q, K, V, O, dO, LSE, scale and causal.
+ *   In: Q, K, V, dO dtype; the workspace.  Out: dK, dV dtype.
+ * workspace: at least fa_bwd_workspace_bytes(...) bytes, 256-byte aligned,
+ *   owned by the caller; what is in it is internal to the library.
+ * Errors as fa_bwd.
+ */
+int fa_bwd_dq_ws(int dtype, int B, int H, int N, int d, const void *Q,
+                 const void *K, const void *V, const void *O, const void *dO,
+                 const float *LSE, float scale, int causal, void *dQ,
+                 void *workspace, size_t workspace_bytes, void *stream);
+int fa_bwd_dkdv_ws(int dtype, int B, int H, int N, int d, const void *Q,
+                   const void *K, const void *V, const void *dO, float scale,
+                   int causal, void *dK, void *dV, const void *workspace,
+                   size_t workspace_bytes, void *stream);
 
 /*
  * fa_bwd without a workspace argument, for callers that cannot allocate
@@ -286,8 +314,9 @@ int fa_bwd_dq(int dtype, int B, int H, int N, int d, const void *Q,
  *   each workgroup forms Dvec for its own query rows from O and dO (the
  *   values fa_bwd_preprocess writes, bit for bit: same products, same
  *   summation tree), uses them and stores them, so that fa_bwd_dkdv can
- *   follow it on the same stream without the preprocess pass. fa_bwd runs
- *   this and then fa_bwd_dkdv.
+ *   follow it on the same stream without the preprocess pass. (fa_bwd runs
+ *   the same sweep as fa_bwd_dq_ws, which also stores each row's scaled LSE
+ *   for the dK/dV sweep.)
  *   In: Q, K, V, O, dO dtype; LSE fp32.  Out: dQ dtype; Dvec [B,H,N] fp32.
  */
 int fa_bwd_dq_d(int dtype, int B, int H, int N, int d, const void *Q,

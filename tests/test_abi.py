@@ -104,6 +104,23 @@ def test_bwd_rejects(L):
     assert _bwd(L, ws_bytes=need - 1) == WS
 
 
+def test_bwd_halves_reject(L):
+    """fa_bwd_dq_ws and fa_bwd_dkdv_ws check their arguments as fa_bwd does,
+    before any HIP call."""
+    need = L.fa_bwd_workspace_bytes(2, 1, 1, 16, 64)
+    dq = lambda dtype=2, N=16, d=64, scale=0.125, causal=0, o=A, lse=A2, dqp=A2, ws=A, wb=need: \
+        L.fa_bwd_dq_ws(dtype, 1, 1, N, d, A, A, A, o, A, lse, scale, causal, dqp, ws, wb, None)
+    kv = lambda dtype=2, N=16, d=64, scale=0.125, causal=0, dk=A2, ws=A, wb=need: \
+        L.fa_bwd_dkdv_ws(dtype, 1, 1, N, d, A, A, A, A, scale, causal, dk, A2, ws, wb, None)
+    for f in (dq, kv):
+        assert f(dtype=0) == UNSUP and f(d=32) == UNSUP
+        assert f(N=0) == INVALID and f(scale=math.inf) == INVALID and f(causal=3) == INVALID
+        assert f(ws=NUL) == INVALID and f(ws=MIS) == INVALID
+        assert f(wb=need - 1) == WS
+    assert dq(o=NUL) == INVALID and dq(lse=NUL) == INVALID and dq(dqp=MIS) == INVALID
+    assert kv(dk=NUL) == INVALID
+
+
 SCRATCH = _status("FA_ERR_SCRATCH")
 MAX_ROWS = 1 << 22   # FA_BWD_NOALLOC_MAX_ROWS
 

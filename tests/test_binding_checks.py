@@ -76,6 +76,15 @@ def test_staged_wrappers_reject_bad_vectors():
             fa.bwd_dq_d(q, q, q, q, q, good, bad, out)
         with pytest.raises(ValueError):
             fa.bwd(q, q, q, q, q, bad)
+        with pytest.raises(ValueError):
+            fa.bwd_dq_ws(q, q, q, q, q, bad, out, torch.zeros(1 << 16, dtype=torch.uint8,
+                                                               device="cuda"))
+    for ws in (None, torch.zeros(16, dtype=torch.uint8, device="cuda"),
+               torch.zeros(1 << 16, dtype=torch.uint8)):
+        with pytest.raises(ValueError):
+            fa.bwd_dq_ws(q, q, q, q, q, good, out, ws)
+        with pytest.raises(ValueError):
+            fa.bwd_dkdv_ws(q, q, q, q, out, out, ws)
     with pytest.raises(ValueError):
         fa.bwd(q, q, q, q, q, good, workspace=torch.zeros(16, dtype=torch.uint8, device="cuda"))
     with pytest.raises(ValueError):

@@ -375,7 +375,8 @@ def test_joint_key_value_permutation(fa):
 
 def test_stages_match_fused_call(fa):
     """fa_bwd equals its three stages called one by one, in either order of
-    the two gradient sweeps, and equals fa_bwd_dq_d then fa_bwd_dkdv; the D
+    the two gradient sweeps, equals fa_bwd_dq_d then fa_bwd_dkdv, and equals
+    its own two launches called apart (fa_bwd_dq_ws, fa_bwd_dkdv_ws); the D
     that fa_bwd_dq_d forms equals fa_bwd_preprocess's bit for bit."""
     w = ai.custom("stages", 2, 4, 700, 128, "bf16", True, seed=11)
     d = _gpu(ai.make_inputs(w))
@@ -397,6 +398,14 @@ def test_stages_match_fused_call(fa):
     torch.cuda.synchronize()
     assert torch.equal(dvec3, dvec)
     assert torch.equal(dk, dk3) and torch.equal(dv, dv3) and torch.equal(dq, dq3)
+    # fa_bwd's two launches as two calls, on a workspace that starts as NaN.
+    ws = torch.full((fa.bwd_workspace_bytes(torch.bfloat16, 2, 4, 700, 128),), 255,
+                    dtype=torch.uint8, device="cuda")
+    dk4, dv4, dq4 = torch.empty_like(dk), torch.empty_like(dv), torch.empty_like(dq)
+    fa.bwd_dq_ws(d["q"], d["k"], d["v"], o, d["do"], lse, dq4, ws, w.scale, True)
+    fa.bwd_dkdv_ws(d["q"], d["k"], d["v"], d["do"], dk4, dv4, ws, w.scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, dk4) and torch.equal(dv, dv4) and torch.equal(dq, dq4)
 
 
 def test_nan_in_query_row_stays_in_that_row(fa):
