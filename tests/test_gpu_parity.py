@@ -199,6 +199,32 @@ def test_eight_wave_blocks_ragged(fa, oracle_lib, causal, N):
     _compare_slices(oracle_lib, w, inp, got, [(0, 0), (3, 15)], True)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_size_independence(fa, causal):
+    """The query-block size is the library's choice (256 rows when the grid
+    has enough such units, else 128) and no row's arithmetic depends on it:
+    a slice computed inside a B4 H16 N4096 batch (256-row blocks in the
+    forward and the dQ sweep) equals the same slice computed alone (128-row
+    blocks), O, LSE, dQ, dK and dV bit for bit."""
+    assert fa_launch_rule(64, 4096, causal) and not fa_launch_rule(1, 4096, causal)
+    w = ai.custom("bs-%s" % ("c" if causal else "nc"), 4, 16, 4096, 128, "bf16", causal, seed=77)
+    inp = ai.make_inputs(w)
+    got = _run(fa, w, inp)
+    for b, h in [(0, 0), (3, 15)]:
+        one = {k: v[b:b + 1, h:h + 1].contiguous() for k, v in inp.items()}
+        w1 = ai.custom("bs-one", 1, 1, 4096, 128, "bf16", causal, seed=77)
+        alone = _run(fa, w1, one)
+        for k in ("o", "lse", "dq", "dk", "dv"):
+            assert torch.equal(alone[k][0, 0], got[k][b, h]), (k, b, h)
+
+
+def fa_launch_rule(BH, N, causal):
+    """The library's rule for 256-row blocks (fa_launch.h, use_256_row_blocks)."""
+    nqb = (N + 255) // 256
+    units = BH * ((nqb + 1) // 2 if causal else nqb)
+    return units >= 256 and (not causal or N >= 4096)
+
+
 @pytest.mark.parametrize("dt,causal", [("bf16", False), ("f16", True)])
 def test_d64_sweep_streams_several_units(fa, oracle_lib, dt, causal):
     """d = 64 with more key-block units than compute units, so that every
