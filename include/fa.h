@@ -42,8 +42,10 @@
  *            argument error nothing is enqueued. FA_ERR_LAUNCH reports a
  *            failed kernel launch (hipGetLastError after the launch); faults
  *            inside a kernel surface at the caller's next synchronisation.
- *            No C++ exception crosses this interface. The library keeps no
- *            state between calls and may be called from several threads.
+ *            No C++ exception crosses this interface. Apart from
+ *            fa_bwd_noalloc's per-device scratch (see there) and a
+ *            thread-safe per-device cache of its address, the library keeps
+ *            no state between calls; it may be called from several threads.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -206,7 +208,10 @@ size_t fa_bwd_workspace_bytes(int dtype, int B, int H, int N, int d);
  *   256-byte aligned, owned by the caller; overwritten (no need to clear it).
  * dtype: FA_F16 and FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED). P and dS
  * are rounded to dtype before the products that consume them; all sums are
- * fp32. Deterministic: the same inputs give bit-identical dQ, dK and dV
+ * fp32. With FA_F16 that rounding bounds |dS| = |P (dP - D)| by the fp16
+ * maximum (65504); dP grows with |dO| |V| sqrt(d), so callers with very
+ * large upstream gradients scale dO down (as loss scaling does), or beyond
+ * the bound the affected gradients become inf or NaN. Deterministic: the same inputs give bit-identical dQ, dK and dV
  * (every output element is summed by one thread in a fixed order).
  * Enqueues fa_bwd_dq_ws (the dQ sweep, which also forms D into the
  * workspace and stores each row's LSE * log2(e) beside it) and then
