@@ -1080,6 +1080,23 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(
   }
 }
 
+// Single blocks in longest-first order, as the forward's fwd_b16_lpt_kernel
+// (causal only).
+template <typename T, int D, bool DFUSE>
+__global__ __launch_bounds__(256, 3) void bwd_dq_lpt_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
+    const uint16_t *__restrict__ O, const float *__restrict__ LSE, float *__restrict__ Dvec,
+    float *__restrict__ L2out, uint16_t *__restrict__ dQ, int N, int nqb, int BH, float c2,
+    float scale) {
+  using C = DqCfg<D, 4>;
+  __shared__ __attribute__((aligned(1024))) uint16_t kv[4 * C::TILE];
+  const int r = blockIdx.x / BH;
+  const int bh = blockIdx.x - r * BH;
+  dq_block<T, D, 4, true, DFUSE>(Q, K, V, dO, O, LSE, Dvec, L2out, dQ, N, bh, nqb - 1 - r, c2,
+                                 scale, kv);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -1163,8 +1180,22 @@ static hipError_t dq_w(const BwdArgs &a, void *dQ, hipStream_t st) {
 
 // Dvec read (a.Dvec) or, with a.O set, formed from O and dO and written to
 // a.Dout.
+template <typename T, int D, bool DFUSE>
+static hipError_t dq_lpt(const BwdArgs &a, void *dQ, hipStream_t st) {
+  using C = DqCfg<D, 4>;
+  const int nqb = (a.N + C::BR - 1) / C::BR;
+  hipLaunchKernelGGL((bwd_dq_lpt_kernel<T, D, DFUSE>), dim3(nqb * a.BH), dim3(C::kThreads), 0,
+                     st, a.Q, a.K, a.V, a.dO, a.O, a.LSE, a.Dout, a.L2out, (uint16_t *)dQ, a.N,
+                     nqb, a.BH, a.c2, a.scale);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t dq(const BwdArgs &a, void *dQ, hipStream_t st) {
+  if constexpr (D == 64 && CAUSAL) {
+    if (use_single_block_order(D, a.N, CAUSAL))
+      return a.O != nullptr ? dq_lpt<T, D, true>(a, dQ, st) : dq_lpt<T, D, false>(a, dQ, st);
+  }
   const bool w8 = use_256_row_blocks(a.BH, a.N, CAUSAL);
   if (a.O != nullptr)
     return w8 ? dq_w<T, D, 8, CAUSAL, true>(a, dQ, st) : dq_w<T, D, 4, CAUSAL, true>(a, dQ, st);

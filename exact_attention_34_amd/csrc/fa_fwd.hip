@@ -478,6 +478,25 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_b16_kernel(
   }
 }
 
+// Single blocks in longest-first order (causal only): workgroup i takes
+// query block nqb - 1 - i / BH of slice i % BH, so the blocks with the most
+// key tiles start first and the short ones fill the tail. Consecutive
+// workgroups go to different XCDs, so each XCD sees the K and V of BH / 8
+// slices at a time.
+template <typename T, int D>
+__global__ __launch_bounds__(256, 3) void fwd_b16_lpt_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int N,
+    int nqb, int BH, float c2) {
+  using C = FwdCfg<D, 4>;
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[C::TILE], K1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[C::TILE], V1[C::TILE];
+  const int r = blockIdx.x / BH;
+  const int bh = blockIdx.x - r * BH;
+  fwd_block<T, D, 4, true, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, nqb - 1 - r, 0,
+                                  N, c2, K0, K1, V0, V1);
+}
+
 // Split-key forward: the keys of every row are cut into nsplit ranges of
 // split_keys keys (a multiple of the tile width), and each (slice, range,
 // query block) is one workgroup, which writes its partial result in fp32:
@@ -907,6 +926,16 @@ static hipError_t fwd_b16_w(int BH, int N, const void *Q, const void *K, const v
 template <typename T, int D, bool CAUSAL>
 static hipError_t fwd_b16(int BH, int N, const void *Q, const void *K, const void *V, float c2,
                           void *O, float *LSE, hipStream_t st) {
+  if constexpr (D == 64 && CAUSAL) {
+    if (use_single_block_order(D, N, CAUSAL)) {
+      using C = FwdCfg<D, 4>;
+      const int nqb = (N + C::BR - 1) / C::BR;
+      hipLaunchKernelGGL((fwd_b16_lpt_kernel<T, D>), dim3(nqb * BH), dim3(C::kThreads), 0, st,
+                         (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                         (uint16_t *)O, LSE, N, nqb, BH, c2);
+      return hipGetLastError();
+    }
+  }
   return use_256_row_blocks(BH, N, CAUSAL)
              ? fwd_b16_w<T, D, 8, CAUSAL>(BH, N, Q, K, V, c2, O, LSE, st)
              : fwd_b16_w<T, D, 4, CAUSAL>(BH, N, Q, K, V, c2, O, LSE, st);

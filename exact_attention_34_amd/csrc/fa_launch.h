@@ -30,6 +30,14 @@ inline bool use_256_row_blocks(int BH, int N, bool causal) {
   return units >= 256 && (!causal || N >= 4096);
 }
 
+// Under the causal mask at d = 64 and N <= 4096 the forward and the dQ sweep
+// take one 128-row query block per workgroup, longest first, at three waves
+// per SIMD, in place of pairs of blocks: pairs leave too few workgroups to
+// keep the chip busy through the tail at these sizes.
+inline bool use_single_block_order(int d, int N, bool causal) {
+  return causal && d == 64 && N <= 4096;
+}
+
 // Split-key forward: key tiles (64 keys) are divided into ranges of
 // split_key_count(N, nsplit) keys, split_parts(N, nsplit) <= nsplit of them,
 // none empty.
