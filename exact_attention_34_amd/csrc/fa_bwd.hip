@@ -1087,14 +1087,13 @@ __global__ __launch_bounds__(256, 3) void bwd_dq_lpt_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const uint16_t *__restrict__ O, const float *__restrict__ LSE, float *__restrict__ Dvec,
-    float *__restrict__ L2out, uint16_t *__restrict__ dQ, int N, int nqb, int BH, float c2,
-    float scale) {
+    float *__restrict__ L2out, uint16_t *__restrict__ dQ, int N, int nqb, int BH, int S,
+    int total, float c2, float scale) {
   using C = DqCfg<D, 4>;
   __shared__ __attribute__((aligned(1024))) uint16_t kv[4 * C::TILE];
-  const int r = blockIdx.x / BH;
-  const int bh = blockIdx.x - r * BH;
-  dq_block<T, D, 4, true, DFUSE>(Q, K, V, dO, O, LSE, Dvec, L2out, dQ, N, bh, nqb - 1 - r, c2,
-                                 scale, kv);
+  int bh, qb;
+  lpt_block(xcd_tile(blockIdx.x, total), nqb, BH, S, bh, qb);
+  dq_block<T, D, 4, true, DFUSE>(Q, K, V, dO, O, LSE, Dvec, L2out, dQ, N, bh, qb, c2, scale, kv);
 }
 
 // ---------------------------------------------------------------------------
@@ -1186,7 +1185,7 @@ static hipError_t dq_lpt(const BwdArgs &a, void *dQ, hipStream_t st) {
   const int nqb = (a.N + C::BR - 1) / C::BR;
   hipLaunchKernelGGL((bwd_dq_lpt_kernel<T, D, DFUSE>), dim3(nqb * a.BH), dim3(C::kThreads), 0,
                      st, a.Q, a.K, a.V, a.dO, a.O, a.LSE, a.Dout, a.L2out, (uint16_t *)dQ, a.N,
-                     nqb, a.BH, a.c2, a.scale);
+                     nqb, a.BH, single_block_group(a.BH, a.N, D), nqb * a.BH, a.c2, a.scale);
   return hipGetLastError();
 }
 

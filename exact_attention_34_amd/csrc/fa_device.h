@@ -129,6 +129,21 @@ __device__ __forceinline__ int xcd_tile(int wg, int total) {
   return (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 
+// Single query blocks in longest-first order over groups of S slices: tile
+// id t (consecutive ids on one XCD, as from xcd_tile) belongs to group
+// t / (S * nqb), whose blocks go longest first across its slices: block
+// nqb - 1 - r of every slice of the group before block nqb - 2 - r. Small
+// groups keep few slices' K and V in an XCD's L2 at a time; the short blocks
+// at the end of each group fill the slots that the long ones leave.
+__device__ __forceinline__ void lpt_block(int t, int nqb, int BH, int S, int &bh, int &qb) {
+  const int s0 = t / (S * nqb) * S;
+  const int ns = min(S, BH - s0);
+  const int k = t - s0 * nqb;
+  const int r = k / ns;
+  bh = s0 + (k - r * ns);
+  qb = nqb - 1 - r;
+}
+
 __device__ __forceinline__ u32x4 ld128(const void *p) { return *(const u32x4 *)p; }
 __device__ __forceinline__ void st128(void *p, const u32x4 &v) { *(u32x4 *)p = v; }
 // Non-temporal 16-byte store (global_store ... nt), for outputs that no

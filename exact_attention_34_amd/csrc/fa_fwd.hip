@@ -478,23 +478,20 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_b16_kernel(
   }
 }
 
-// Single blocks in longest-first order (causal only): workgroup i takes
-// query block nqb - 1 - i / BH of slice i % BH, so the blocks with the most
-// key tiles start first and the short ones fill the tail. Consecutive
-// workgroups go to different XCDs, so each XCD sees the K and V of BH / 8
-// slices at a time.
+// Single blocks in longest-first order over groups of S slices (causal
+// only; lpt_block), one 128-row block per workgroup.
 template <typename T, int D>
 __global__ __launch_bounds__(256, 3) void fwd_b16_lpt_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int N,
-    int nqb, int BH, float c2) {
+    int nqb, int BH, int S, int total, float c2) {
   using C = FwdCfg<D, 4>;
   __shared__ __attribute__((aligned(1024))) uint16_t K0[C::TILE], K1[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t V0[C::TILE], V1[C::TILE];
-  const int r = blockIdx.x / BH;
-  const int bh = blockIdx.x - r * BH;
-  fwd_block<T, D, 4, true, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, nqb - 1 - r, 0,
-                                  N, c2, K0, K1, V0, V1);
+  int bh, qb;
+  lpt_block(xcd_tile(blockIdx.x, total), nqb, BH, S, bh, qb);
+  fwd_block<T, D, 4, true, false>(Q, K, V, O, LSE, nullptr, nullptr, N, N, 0, bh, qb, 0, N, c2,
+                                  K0, K1, V0, V1);
 }
 
 // Split-key forward: the keys of every row are cut into nsplit ranges of
@@ -932,7 +929,8 @@ static hipError_t fwd_b16(int BH, int N, const void *Q, const void *K, const voi
       const int nqb = (N + C::BR - 1) / C::BR;
       hipLaunchKernelGGL((fwd_b16_lpt_kernel<T, D>), dim3(nqb * BH), dim3(C::kThreads), 0, st,
                          (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                         (uint16_t *)O, LSE, N, nqb, BH, c2);
+                         (uint16_t *)O, LSE, N, nqb, BH, single_block_group(BH, N, D), nqb * BH,
+                         c2);
       return hipGetLastError();
     }
   }

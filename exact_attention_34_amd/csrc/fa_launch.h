@@ -37,6 +37,13 @@ inline bool use_256_row_blocks(int BH, int N, bool causal) {
 inline bool use_single_block_order(int d, int N, bool causal) {
   return causal && d == 64 && N <= 4096;
 }
+// Slices per group of that order: as many as keep the group's K and V
+// within 4 MiB (one XCD's L2), at least one.
+inline int single_block_group(int BH, int N, int d) {
+  const long per_slice = 4L * N * d;  // K and V, 16-bit
+  const long s = (4L << 20) / per_slice;
+  return (int)(s < 1 ? 1 : s > BH ? BH : s);
+}
 
 // Split-key forward: key tiles (64 keys) are divided into ranges of
 // split_key_count(N, nsplit) keys, split_parts(N, nsplit) <= nsplit of them,
