@@ -225,6 +225,45 @@ def fa_launch_rule(BH, N, causal):
     return units >= 256 and (not causal or N >= 4096)
 
 
+def single_block_rule(d, N, causal):
+    """The library's rule for single query blocks in longest-first order
+    (fa_launch.h, use_single_block_order), and its slices per group
+    (single_block_group)."""
+    return causal and d == 64 and N <= 4096
+
+
+def single_block_group(BH, N, d):
+    return max(1, min(BH, (4 << 20) // (4 * N * d)))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_single_block_order_groups(fa, oracle_lib, dt):
+    """Causal d = 64, N = 2000: the forward and the dQ sweep take single
+    query blocks longest first over groups of 8 slices; B3 H7 gives groups of
+    8, 8 and 5 slices, so the last group is short. Slices at the ends of every
+    group against the oracle."""
+    B, H, N = 3, 7, 2000
+    S = single_block_group(B * H, N, 64)
+    assert single_block_rule(64, N, True) and S == 8 and (B * H) % S != 0
+    w = ai.custom("lpt-groups-%s" % dt, B, H, N, 64, dt, True, seed=31)
+    inp = ai.make_inputs(w)
+    got = _run(fa, w, inp)
+    ends = sorted({i for g0 in range(0, B * H, S) for i in (g0, min(g0 + S, B * H) - 1)})
+    _compare_slices(oracle_lib, w, inp, got, [divmod(i, H) for i in ends], True)
+
+
+@pytest.mark.parametrize("N", [4096, 4097])
+def test_single_block_rule_boundary(fa, oracle_lib, N):
+    """Causal d = 64 on both sides of the single-block rule (N = 4096 single
+    blocks in longest-first order, N = 4097 pairs of blocks with a one-row
+    last block): two slices against the oracle."""
+    assert single_block_rule(64, N, True) == (N == 4096)
+    w = ai.custom("lpt-edge-%d" % N, 2, 2, N, 64, "f16", True, seed=47)
+    inp = ai.make_inputs(w)
+    got = _run(fa, w, inp)
+    _compare_slices(oracle_lib, w, inp, got, [(0, 0), (1, 1)], True)
+
+
 @pytest.mark.parametrize("dt,causal", [("bf16", False), ("f16", True)])
 def test_d64_sweep_streams_several_units(fa, oracle_lib, dt, causal):
     """d = 64 with more key-block units than compute units, so that every
