@@ -1,7 +1,9 @@
-"""Tensors past 4 GiB: B41 H400 N1024 d128 bf16 holds 2^31 + 2^21 elements per
-tensor, so the last 16 slices start beyond element 2^31 (byte 4 GiB). Forward
-and backward run on the whole batch; slices on both sides of that boundary are
-compared with the fp64 oracle (parity_utils tolerances)."""
+"""Tensors past 2^31 elements: B41 H400 N1024 d128 bf16 and B41 H800 N1024
+d64 fp16 hold 2^31 + 2^21 elements per tensor, so the last slices start beyond
+element 2^31. Forward and backward run on the whole batch; slices on both
+sides of that boundary are compared with the fp64 oracle (parity_utils
+tolerances). The causal d = 64 case runs the forward and the dQ sweep as
+single query blocks in longest-first order over groups of 16 slices."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +13,10 @@ from parity_utils import check_fwd, check_grads, f64
 
 pytestmark = pytest.mark.gpu
 
-SLICES = [0, 16383, 16384, 16399]  # (b, h) flattened; 16384 * 2^17 = 2^31
+# (B, H, N, d, dtype) and the (b, h) slices compared, flattened: slice s
+# starts at element s * N * d, which is 2^31 for s = 2^31 / (N d).
+SHAPES = {"d128": (41, 400, 1024, 128, "bf16", [0, 16383, 16384, 16399]),
+          "d64": (41, 800, 1024, 64, "f16", [0, 32767, 32768, 32799])}
 
 
 @pytest.fixture(scope="module")
@@ -22,13 +27,16 @@ def fa():
     return fa
 
 
+@pytest.mark.parametrize("shape", ["d128", "d64"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_tensors_past_4gib(fa, oracle_lib, causal):
+def test_tensors_past_4gib(fa, oracle_lib, causal, shape):
     if torch.cuda.get_device_properties(0).total_memory < (96 << 30):
         pytest.skip("needs about 45 GiB of device memory")
-    w = ai.custom("large-%s" % ("c" if causal else "nc"), 41, 400, 1024, 128, "bf16", causal,
+    B, H, N, d, dt, SLICES = SHAPES[shape]
+    w = ai.custom("large-%s-%s" % (shape, "c" if causal else "nc"), B, H, N, d, dt, causal,
                   seed=4000 + int(causal))
     assert w.B * w.H * w.N * w.d > 2 ** 31
+    assert SLICES[1] * N * d < 2 ** 31 <= SLICES[2] * N * d
     inp = ai.make_inputs_device(w)
     o, lse = fa.fwd(inp["q"], inp["k"], inp["v"], w.scale, causal)
     dq, dk, dv = fa.bwd(inp["q"], inp["k"], inp["v"], o, inp["do"], lse, w.scale, causal)
