@@ -438,12 +438,17 @@ def test_joint_key_value_permutation(fa):
         assert r <= 1e-2, (key, r)
 
 
-def test_stages_match_fused_call(fa):
+@pytest.mark.parametrize("hd,dt", [(128, "bf16"), (64, "f16")])
+def test_stages_match_fused_call(fa, hd, dt):
     """fa_bwd equals its three stages called one by one, in either order of
     the two gradient sweeps, equals fa_bwd_dq_d then fa_bwd_dkdv, and equals
     its own two launches called apart (fa_bwd_dq_ws, fa_bwd_dkdv_ws); the D
-    that fa_bwd_dq_d forms equals fa_bwd_preprocess's bit for bit."""
-    w = ai.custom("stages", 2, 4, 700, 128, "bf16", True, seed=11)
+    that fa_bwd_dq_d forms equals fa_bwd_preprocess's bit for bit. At d = 64
+    (causal, N <= 4096) the dQ sweeps are the single-block kernels, both the
+    one forming D and the one reading it."""
+    if hd == 64:
+        assert single_block_rule(64, 700, True)
+    w = ai.custom("stages-d%d" % hd, 2, 4, 700, hd, dt, True, seed=11)
     d = _gpu(ai.make_inputs(w))
     o, lse = fa.fwd(d["q"], d["k"], d["v"], w.scale, True)
     dq, dk, dv = fa.bwd(d["q"], d["k"], d["v"], o, d["do"], lse, w.scale, True)
@@ -464,7 +469,7 @@ def test_stages_match_fused_call(fa):
     assert torch.equal(dvec3, dvec)
     assert torch.equal(dk, dk3) and torch.equal(dv, dv3) and torch.equal(dq, dq3)
     # fa_bwd's two launches as two calls, on a workspace that starts as NaN.
-    ws = torch.full((fa.bwd_workspace_bytes(torch.bfloat16, 2, 4, 700, 128),), 255,
+    ws = torch.full((fa.bwd_workspace_bytes(d["q"].dtype, 2, 4, 700, w.d),), 255,
                     dtype=torch.uint8, device="cuda")
     dk4, dv4, dq4 = torch.empty_like(dk), torch.empty_like(dv), torch.empty_like(dq)
     fa.bwd_dq_ws(d["q"], d["k"], d["v"], o, d["do"], lse, dq4, ws, w.scale, True)
