@@ -39,6 +39,7 @@ def _noalloc(fa, d, o, lse, w, outs):
 @pytest.mark.parametrize("first,second", [
     (("big", 4, 8, 1500, 128, "bf16", True), ("small", 1, 3, 333, 128, "bf16", True)),
     (("big64", 2, 16, 2048, 64, "f16", False), ("small64", 1, 1, 70, 64, "f16", False)),
+    (("big64c", 2, 8, 2000, 64, "bf16", True), ("small64c", 1, 2, 300, 64, "bf16", True)),
 ])
 def test_noalloc_matches_fa_bwd(fa, oracle_lib, first, second):
     for i, spec in enumerate((first, second)):
